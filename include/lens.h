@@ -1,0 +1,200 @@
+/*
+ * lens.h -- C ABI of the MI355X (gfx950) Lens MM-DiT denoiser library.
+ *
+ * The library runs the forward pass of the Lens double-stream MM-DiT
+ * denoiser (48 blocks, hidden 1536 = 24 heads x 64, separate image and text
+ * weights, per-stream AdaLN, RMSNorm + modulation, QK RMSNorm, 3-axis RoPE,
+ * joint text+image attention, gated SwiGLU MLP) and the flow-matching Euler
+ * step with classifier-free guidance, on hand-written HIP kernels.
+ *
+ * Sources, by page and section:
+ *   Lens blog post (zjwfufu.github.io), "Overview": 48 blocks, hidden 1536,
+ *     24 heads, gated MLP 1536x4096, per-stream AdaLN 1536x9216 giving a
+ *     shift/scale/gate triple before attention and another before the MLP;
+ *     "Exploring Text Encoder": zero-padded text is masked out of the DiT;
+ *     "Exploring Image Editing": the CFG combination.
+ *   Lens-Turbo-3.8B-bf16 article (wmrh.cn): per-block tensors img_qkv /
+ *     txt_qkv, norm_q / norm_k / norm_added_q / norm_added_k, to_out /
+ *     to_add_out, img_mod / txt_mod, img_mlp / txt_mlp w1 w2 w3; rms_norm;
+ *     axes_dims_rope [8, 28, 28]; in_channels 128 (2x2 patches of 32
+ *     channels); txt_norm.0..3; norm_out.linear and proj_out.
+ *   "Lens: Rethinking Training Efficiency ..." summary, 前置知识: the flow
+ *     matching path x_t = (1 - t) x0 + t x1 and its velocity target.
+ *   SOTA image generation survey (youngju.dev), "CFG" and "Rectified Flow".
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  Config and
+ *     weight-table structs are HOST memory, read only during the call.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  A return of LENS_OK means "enqueued":
+ *     no device synchronisation is done.
+ *   - Argument checks are synchronous; a failure returns a negative status
+ *     and sets a thread-local message readable with lens_last_error().
+ *     Nothing is enqueued when a check fails.
+ *   - The library allocates no device memory; scratch space is the caller's
+ *     workspace, sized by the *_workspace_bytes functions (256-byte aligned).
+ *   - Matrices are row-major.  A Linear layer's weight is [out, in] (the
+ *     input dimension contiguous) and its bias is [out] or NULL.
+ *   - Activation / weight element type is cfg->act_dtype (LENS_BF16 or
+ *     LENS_F32); residual streams, the timestep embedding, latents x (in the
+ *     flow step) and the velocity v are always float32.  bf16 is stored as
+ *     IEEE bfloat16 bit patterns, rounded to nearest even.
+ */
+#ifndef LENS_H
+#define LENS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LENS_OK = 0,
+  LENS_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, inconsistent config */
+  LENS_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim != 64) */
+  LENS_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than required */
+  LENS_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} lens_status;
+
+typedef enum { LENS_F32 = 0, LENS_BF16 = 1 } lens_dtype;
+
+/* Model configuration; lens_default_config() fills the Lens values. */
+typedef struct {
+  int32_t hidden;       /* 1536 = heads * head_dim */
+  int32_t heads;        /* 24 */
+  int32_t head_dim;     /* 64 (the only supported value) */
+  int32_t mlp_hidden;   /* 4096 */
+  int32_t n_blocks;     /* 48 */
+  int32_t rope_axes[3]; /* 8, 28, 28: even, summing to head_dim */
+  int32_t in_ch;        /* 128 features per patchified image token */
+  int32_t out_ch;       /* 128 */
+  int32_t txt_feat_dim; /* 2880 per encoder layer */
+  int32_t txt_layers;   /* 4 */
+  int32_t t_freq_dim;   /* 256 sinusoidal timestep features */
+  float rope_theta;     /* 10000 */
+  float eps;            /* 1e-6, all RMSNorms */
+  float t_scale;        /* 1000: the sinusoid sees t_scale * t */
+  lens_dtype act_dtype; /* element type of weights and activations */
+} lens_config;
+
+/* One Linear layer: w [out, in] in act_dtype, b [out] in act_dtype or NULL. */
+typedef struct {
+  const void *w;
+  const void *b;
+} lens_linear;
+
+/* Weights of one stream of one block.  q_gain / k_gain: [head_dim] gains of
+ * the per-head RMSNorm of q and k (norm_q / norm_k for the image stream,
+ * norm_added_q / norm_added_k for the text stream).  mod: 6*hidden outputs in
+ * the order shift1, scale1, gate1, shift2, scale2, gate2.  qkv: 3*hidden
+ * outputs q | k | v, each heads x head_dim.  w1 = gate, w3 = up, w2 = down. */
+typedef struct {
+  lens_linear mod, qkv, out, w1, w3, w2;
+  const void *q_gain, *k_gain;
+} lens_stream_w;
+
+typedef struct {
+  lens_stream_w img, txt;
+} lens_block_w;
+
+/* Non-block weights.  t_fc1: [hidden, t_freq_dim]; t_fc2: [hidden, hidden];
+ * img_in: [hidden, in_ch]; txt_gain: [txt_layers, txt_feat_dim] (one
+ * device array); txt_in: [hidden, txt_layers * txt_feat_dim]; norm_out:
+ * [2*hidden, hidden] giving shift then scale; proj_out: [out_ch, hidden].
+ * blocks: HOST array of n_blocks block tables, run in array order. */
+typedef struct {
+  lens_linear t_fc1, t_fc2, img_in, txt_in, norm_out, proj_out;
+  const void *txt_gain;
+  const lens_block_w *blocks;
+} lens_dit_w;
+
+/* Fills *cfg with the Lens configuration and the given activation type. */
+void lens_default_config(lens_config *cfg, lens_dtype act_dtype);
+
+/* Bytes of workspace lens_block_forward / lens_dit_forward need for batch B,
+ * S_img image tokens and S_txt text tokens; 0 if the arguments are invalid. */
+size_t lens_block_workspace_bytes(const lens_config *cfg, int32_t B, int32_t S_img, int32_t S_txt);
+size_t lens_dit_workspace_bytes(const lens_config *cfg, int32_t B, int32_t S_img, int32_t S_txt);
+
+/*
+ * One double-stream block, in place on the residual streams.
+ *   h_img [B, S_img, hidden] f32, h_txt [B, S_txt, hidden] f32: updated.
+ *   temb  [B, hidden] f32: timestep embedding; AdaLN is computed inside as
+ *         mod = W_mod . SiLU(temb) + b_mod for each stream.
+ *   img_pos [S_img, 3], txt_pos [S_txt, 3] int32 RoPE positions (the same
+ *         for every sample of the batch).
+ *   txt_len [B] int32 valid text lengths (device), or NULL = all S_txt valid.
+ *         Text keys j >= txt_len[b] are masked; values are clamped to
+ *         [0, S_txt].  Rows of masked text queries are computed but their
+ *         values are unspecified.
+ * Per stream: a = RMSNorm(h)(1 + scale1) + shift1; qkv = a W_qkv^T + b;
+ * q, k <- RMSNorm_64(.) * gain, then RoPE; joint softmax attention of each
+ * sample's image and text queries over all of its valid keys, scale
+ * 1/sqrt(head_dim); h += gate1 (O W_out^T + b); a = RMSNorm(h)(1 + scale2)
+ * + shift2; h += gate2 (W2 (SiLU(W1 a + b1) (W3 a + b3)) + b2).
+ * Requires B >= 1, S_img >= 1, S_txt >= 0.
+ */
+lens_status lens_block_forward(const lens_config *cfg, const lens_block_w *w, float *h_img, float *h_txt,
+                               const float *temb, const int32_t *img_pos, const int32_t *txt_pos,
+                               const int32_t *txt_len, int32_t B, int32_t S_img, int32_t S_txt,
+                               void *workspace, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Whole denoiser: v = proj_out(norm_out(blocks(img_in(x), txt_in(f)), temb)).
+ *   x         [B, S_img, in_ch] act_dtype: patchified latent tokens (read only).
+ *   txt_feats [B, S_txt, txt_layers * txt_feat_dim] act_dtype, layer-major.
+ *   t         [B] f32 timesteps (device).
+ *   positions and txt_len as for lens_block_forward.
+ *   v_out     [B, S_img, out_ch] f32 velocity.
+ * temb = t_fc2(SiLU(t_fc1(phi(t)))), phi(t) = [cos(t_scale t w_k) | sin(...)],
+ * w_k = 10000^(-k / (t_freq_dim/2)); the text input is RMSNorm(layer) *
+ * txt_gain[layer] for each layer, concatenated, then txt_in.  The final layer
+ * computes (shift, scale) = norm_out(SiLU(temb)) and v = proj_out(
+ * RMSNorm(h_img)(1 + scale) + shift).
+ * For classifier-free guidance put the cond samples in [0, n) and the uncond
+ * samples in [n, 2n) of one batch (x and t duplicated) and pass the two halves
+ * of v_out to lens_flow_step.
+ */
+lens_status lens_dit_forward(const lens_config *cfg, const lens_dit_w *w, const void *x, const void *txt_feats,
+                             const float *t, const int32_t *img_pos, const int32_t *txt_pos,
+                             const int32_t *txt_len, int32_t B, int32_t S_img, int32_t S_txt, float *v_out,
+                             void *workspace, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Flow-matching Euler step with optional classifier-free guidance, on n
+ * elements:  v = v_uncond + cfg_scale (v_cond - v_uncond)  (v = v_cond when
+ * v_uncond is NULL);  x <- x + dt v.  x f32 is updated in place; v_cond and
+ * v_uncond are f32.  If x_lowp_out is not NULL it receives the new x in
+ * lowp_dtype (the input of the next lens_dit_forward).  n >= 0.
+ */
+lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond, int64_t n, float dt,
+                           float cfg_scale, void *x_lowp_out, lens_dtype lowp_dtype, void *hip_stream);
+
+/*
+ * Opt-in kernel timer for measurement.  lens_timer_start(kind) makes every
+ * later launch of that kernel family (see lens_kernel_kind) on any stream
+ * record HIP events around itself; lens_timer_stop() synchronises those
+ * events, returns the summed kernel milliseconds and the launch count, and
+ * switches the timer off.  Not thread-safe; meant for a single benchmark
+ * thread.
+ */
+typedef enum {
+  LENS_KERNEL_GEMM = 0,      /* bf16 MFMA GEMM (all projections) */
+  LENS_KERNEL_ATTENTION = 1, /* joint flash attention */
+  LENS_KERNEL_NORM = 2,      /* RMSNorm + modulation */
+  LENS_KERNEL_QKNORM_ROPE = 3,
+  LENS_KERNEL_ADALN = 4      /* skinny GEMV (AdaLN, timestep MLP) */
+} lens_kernel_kind;
+lens_status lens_timer_start(lens_kernel_kind kind);
+lens_status lens_timer_stop(double *total_ms, int64_t *launches);
+
+const char *lens_status_string(lens_status s);
+const char *lens_last_error(void);
+const char *lens_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LENS_H */

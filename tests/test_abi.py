@@ -1,0 +1,127 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, fills the Lens config, sizes workspaces, and rejects bad arguments
+before touching the GPU (no compute call is made here)."""
+import ctypes as C
+import json
+import os
+import re
+
+import pytest
+
+import text_image_flow_amd as T
+from text_image_flow_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lens.h")
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "lens_config.json")))
+
+
+def header_functions():
+    txt = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return set(re.findall(r"\b(lens_[a-z_0-9]+)\s*\(", txt))
+
+
+def test_library_exports_every_header_function():
+    names = header_functions()
+    assert names == set(L.EXPORTS), names ^ set(L.EXPORTS)
+    lib = C.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_default_config_matches_pages():
+    c = T.default_config(T.LENS_BF16)
+    g = lambda k: GOLD[k]["value"]
+    assert (c.n_blocks, c.hidden, c.heads, c.head_dim) == (g("n_blocks"), g("hidden"), g("heads"), g("head_dim"))
+    assert list(c.rope_axes) == g("rope_axes") and c.mlp_hidden == g("mlp_hidden")
+    assert c.in_ch == g("in_channels") and c.txt_feat_dim == g("enc_hidden_dim") and c.txt_layers == g("txt_layers")
+    assert c.act_dtype == T.LENS_BF16 and T.default_config(T.LENS_F32).act_dtype == T.LENS_F32
+    assert "gfx950" in T.version()
+
+
+def test_status_strings():
+    for s, n in [(0, "LENS_OK"), (-1, "LENS_ERR_INVALID_ARG"), (-2, "LENS_ERR_UNSUPPORTED"),
+                 (-3, "LENS_ERR_WORKSPACE"), (-4, "LENS_ERR_HIP")]:
+        assert T.status_string(s) == n
+
+
+def test_workspace_sizes():
+    c = T.default_config(T.LENS_BF16)
+    a = T.lens_block_workspace_bytes(c, 1, 4096, 512)
+    b = T.lens_block_workspace_bytes(c, 2, 4096, 512)
+    assert a > 0 and b > a and a % 256 == 0
+    f = T.default_config(T.LENS_F32)
+    assert T.lens_block_workspace_bytes(f, 1, 4096, 512) > a           # 4-byte activations
+    assert T.lens_dit_workspace_bytes(c, 2, 4096, 512) > b
+    assert T.lens_block_workspace_bytes(c, 0, 4096, 512) == 0           # invalid sizes
+    assert T.lens_block_workspace_bytes(c, 1, 0, 512) == 0
+    assert T.lens_block_workspace_bytes(c, 1, 16, 0) > 0                # no text is valid
+
+
+def _bad(cfg_mut=None, **kw):
+    c = T.default_config(T.LENS_BF16)
+    if cfg_mut:
+        cfg_mut(c)
+    w = T.LensBlockW()
+    for s in ("img", "txt"):
+        sw = getattr(w, s)
+        for n in ("mod", "qkv", "out", "w1", "w3", "w2"):
+            getattr(sw, n).w = 0x1000
+        sw.q_gain = sw.k_gain = 0x1000
+    args = dict(h_img=0x1000, h_txt=0x1000, temb=0x1000, img_pos=0x1000, txt_pos=0x1000, txt_len=None,
+                B=1, S_img=16, S_txt=8, ws=0x1000, ws_bytes=1 << 40)
+    args.update(kw)
+    st = T.lens_block_forward(c, w, args["h_img"], args["h_txt"], args["temb"], args["img_pos"], args["txt_pos"],
+                              args["txt_len"], args["B"], args["S_img"], args["S_txt"], args["ws"],
+                              args["ws_bytes"], None)
+    return st, T.last_error()
+
+
+@pytest.mark.parametrize("mut,kw,status,frag", [
+    (lambda c: setattr(c, "head_dim", 32), {}, L.LENS_ERR_INVALID_ARG, "hidden"),
+    (lambda c: (setattr(c, "heads", 48), setattr(c, "head_dim", 32),
+                c.rope_axes.__setitem__(0, 4), c.rope_axes.__setitem__(1, 14), c.rope_axes.__setitem__(2, 14)),
+     {}, L.LENS_ERR_UNSUPPORTED, "head_dim"),
+    (lambda c: c.rope_axes.__setitem__(0, 7), {}, L.LENS_ERR_INVALID_ARG, "rope_axes"),
+    (lambda c: setattr(c, "act_dtype", 7), {}, L.LENS_ERR_INVALID_ARG, "act_dtype"),
+    (None, {"B": 0}, L.LENS_ERR_INVALID_ARG, "B >= 1"),
+    (None, {"S_img": 0}, L.LENS_ERR_INVALID_ARG, "S_img"),
+    (None, {"S_txt": -1}, L.LENS_ERR_INVALID_ARG, "S_txt"),
+    (None, {"h_img": None}, L.LENS_ERR_INVALID_ARG, "NULL"),
+    (None, {"ws_bytes": 100}, L.LENS_ERR_WORKSPACE, "workspace"),
+    (None, {"ws": None}, L.LENS_ERR_WORKSPACE, "workspace"),
+    (None, {"ws": 0x1001}, L.LENS_ERR_WORKSPACE, "aligned"),
+])
+def test_block_forward_argument_checks(mut, kw, status, frag):
+    st, msg = _bad(mut, **kw)
+    assert st == status and frag in msg, (st, msg)
+
+
+def test_null_weight_is_rejected():
+    c = T.default_config(T.LENS_BF16)
+    w = T.LensBlockW()
+    st = T.lens_block_forward(c, w, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 1, 16, 8, 0x1000, 1 << 40, None)
+    assert st == L.LENS_ERR_INVALID_ARG and "NULL" in T.last_error()
+    st = L.lib().lens_block_forward(None, None, None, None, None, None, None, None, 1, 1, 1, None, 0, None)
+    assert st == L.LENS_ERR_INVALID_ARG and "cfg" in T.last_error()
+
+
+def test_dit_and_flow_argument_checks():
+    c = T.default_config(T.LENS_BF16)
+    d = T.LensDitW()
+    st = T.lens_dit_forward(c, d, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 1, 16, 8, 0x1000, 0x1000, 1 << 40,
+                            None)
+    assert st == L.LENS_ERR_INVALID_ARG and "t_fc1" in T.last_error()
+    c2 = T.default_config(T.LENS_BF16)
+    c2.out_ch = 96
+    assert T.lens_dit_workspace_bytes(c2, 1, 16, 8) == 0
+    assert T.lens_flow_step(None, None, None, -1, 0.1, 1.0, None, 1, None) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_flow_step(None, None, None, 5, 0.1, 1.0, None, 1, None) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_flow_step(0x1000, 0x1000, None, 5, 0.1, 1.0, 0x1000, 9, None) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_flow_step(None, None, None, 0, 0.1, 1.0, None, 1, None) == L.LENS_OK   # empty: nothing to do
+
+
+def test_timer_argument_check():
+    assert T.lens_timer_start(99) == L.LENS_ERR_INVALID_ARG
+    st, ms, n = T.lens_timer_stop()
+    assert st == L.LENS_OK and n == 0 and ms == 0.0

@@ -1,0 +1,517 @@
+// C-ABI layer of the Lens denoiser library: argument checks, workspace
+// carve-up and the launch sequences of one block, the whole denoiser and
+// the flow step.  Host code only; every arithmetic step runs in the kernels.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/lens.h"
+#include "common.h"
+
+using namespace lens;
+
+namespace {
+
+thread_local std::string g_err;
+
+lens_status fail(lens_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+lens_status fail(lens_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+// ------------------------------------------------------------ kernel timer
+struct Timer {
+  int kind = -1;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+} g_timer;
+
+// Wraps one launch: records events around it when its family is timed.
+struct Timed {
+  bool on;
+  hipStream_t st;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  Timed(lens_kernel_kind k, hipStream_t s) : on(g_timer.kind == (int)k), st(s) {
+    if (!on) return;
+    while (g_timer.pool.size() < g_timer.used + 2) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) {
+        on = false;
+        return;
+      }
+      g_timer.pool.push_back(e);
+    }
+    e0 = g_timer.pool[g_timer.used++];
+    e1 = g_timer.pool[g_timer.used++];
+    (void)hipEventRecord(e0, st);
+  }
+  hipError_t done(hipError_t e) {
+    if (on) (void)hipEventRecord(e1, st);
+    return e;
+  }
+};
+
+#define HIP_TRY(expr)                                                                           \
+  do {                                                                                          \
+    hipError_t _e = (expr);                                                                     \
+    if (_e != hipSuccess) return fail(LENS_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------ checks
+lens_status check_config(const lens_config *c) {
+  if (!c) return fail(LENS_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->act_dtype != LENS_F32 && c->act_dtype != LENS_BF16)
+    return fail(LENS_ERR_INVALID_ARG, "act_dtype %d is not LENS_F32 or LENS_BF16", (int)c->act_dtype);
+  if (c->heads <= 0 || c->head_dim <= 0 || c->hidden != c->heads * c->head_dim)
+    return fail(LENS_ERR_INVALID_ARG, "hidden (%d) must equal heads (%d) * head_dim (%d)", c->hidden, c->heads,
+                c->head_dim);
+  const int *ax = c->rope_axes;
+  if (ax[0] < 0 || ax[1] < 0 || ax[2] < 0 || ax[0] % 2 || ax[1] % 2 || ax[2] % 2 ||
+      ax[0] + ax[1] + ax[2] != c->head_dim)
+    return fail(LENS_ERR_INVALID_ARG, "rope_axes (%d,%d,%d) must be even and sum to head_dim %d", ax[0], ax[1],
+                ax[2], c->head_dim);
+  if (c->head_dim != 64) return fail(LENS_ERR_UNSUPPORTED, "head_dim %d: only 64 is supported", c->head_dim);
+  if (c->hidden % 256 || c->hidden > 2048)
+    return fail(LENS_ERR_UNSUPPORTED, "hidden %d: must be a multiple of 256, at most 2048", c->hidden);
+  if (c->mlp_hidden <= 0 || c->mlp_hidden % 128)
+    return fail(LENS_ERR_UNSUPPORTED, "mlp_hidden %d: must be a positive multiple of 128", c->mlp_hidden);
+  if (!(c->eps > 0.f) || !(c->rope_theta > 0.f))
+    return fail(LENS_ERR_INVALID_ARG, "eps and rope_theta must be positive");
+  return LENS_OK;
+}
+
+lens_status check_dit_config(const lens_config *c) {
+  lens_status s = check_config(c);
+  if (s != LENS_OK) return s;
+  if (c->n_blocks < 0) return fail(LENS_ERR_INVALID_ARG, "n_blocks %d < 0", c->n_blocks);
+  if (c->in_ch <= 0 || c->in_ch % 64)
+    return fail(LENS_ERR_UNSUPPORTED, "in_ch %d: must be a positive multiple of 64", c->in_ch);
+  if (c->out_ch <= 0 || c->out_ch % 128)
+    return fail(LENS_ERR_UNSUPPORTED, "out_ch %d: must be a positive multiple of 128", c->out_ch);
+  if (c->txt_layers <= 0 || c->txt_feat_dim <= 0 || (c->txt_layers * c->txt_feat_dim) % 64)
+    return fail(LENS_ERR_UNSUPPORTED, "txt_layers * txt_feat_dim must be a positive multiple of 64");
+  if (c->t_freq_dim <= 0 || c->t_freq_dim % 16)
+    return fail(LENS_ERR_UNSUPPORTED, "t_freq_dim %d: must be a positive multiple of 16", c->t_freq_dim);
+  return LENS_OK;
+}
+
+lens_status check_sizes(int B, int Si, int St) {
+  if (B < 1 || Si < 1 || St < 0)
+    return fail(LENS_ERR_INVALID_ARG, "need B >= 1, S_img >= 1, S_txt >= 0 (got %d, %d, %d)", B, Si, St);
+  if ((int64_t)Si + St > (1 << 24)) return fail(LENS_ERR_UNSUPPORTED, "sequence too long");
+  return LENS_OK;
+}
+
+lens_status check_linear(const lens_linear &l, const char *name) {
+  if (!l.w) return fail(LENS_ERR_INVALID_ARG, "weight %s is NULL", name);
+  return LENS_OK;
+}
+
+lens_status check_block_w(const lens_block_w *w, int idx) {
+  if (!w) return fail(LENS_ERR_INVALID_ARG, "block %d weight table is NULL", idx);
+  const lens_stream_w *s[2] = {&w->img, &w->txt};
+  const char *nm[2] = {"img", "txt"};
+  for (int i = 0; i < 2; ++i) {
+    const lens_linear *ls[6] = {&s[i]->mod, &s[i]->qkv, &s[i]->out, &s[i]->w1, &s[i]->w3, &s[i]->w2};
+    const char *ln[6] = {"mod", "qkv", "out", "w1", "w3", "w2"};
+    for (int j = 0; j < 6; ++j)
+      if (!ls[j]->w) return fail(LENS_ERR_INVALID_ARG, "block %d %s.%s weight is NULL", idx, nm[i], ln[j]);
+    if (!s[i]->q_gain || !s[i]->k_gain)
+      return fail(LENS_ERR_INVALID_ARG, "block %d %s q/k gain is NULL", idx, nm[i]);
+  }
+  return LENS_OK;
+}
+
+// ------------------------------------------------------------ workspace
+struct BlockWs {
+  float *mod;                 // [2][B][6D]
+  void *a_img, *a_txt;        // [B*S, D] act: norm output, then attention output
+  void *qkv_img, *qkv_txt;    // [B*S, 3D] act; reused for the SwiGLU output [B*S, mlp]
+  void *Q, *K, *Vt;           // joint layout
+  size_t bytes;
+};
+
+int s_pad(int Si, int St) { return ((Si + St + 63) / 64) * 64; }
+
+BlockWs carve_block(const lens_config *c, int B, int Si, int St, char *base, bool with_mod) {
+  const size_t es = c->act_dtype == LENS_BF16 ? 2 : 4;
+  const size_t D = c->hidden;
+  const size_t wide = 3 * D > (size_t)c->mlp_hidden ? 3 * D : (size_t)c->mlp_hidden;
+  const size_t Sp = s_pad(Si, St);
+  BlockWs w{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    void *p = base ? base + off : nullptr;
+    off += align_up(n);
+    return p;
+  };
+  w.mod = with_mod ? (float *)take(2 * (size_t)B * 6 * D * 4) : nullptr;
+  w.a_img = take((size_t)B * Si * D * es);
+  w.a_txt = take((size_t)B * St * D * es);
+  w.qkv_img = take((size_t)B * Si * wide * es);
+  w.qkv_txt = take((size_t)B * St * wide * es);
+  w.Q = take((size_t)B * c->heads * Sp * 64 * es);
+  w.K = take((size_t)B * c->heads * Sp * 64 * es);
+  w.Vt = take((size_t)B * c->heads * Sp * 64 * es);
+  w.bytes = off;
+  return w;
+}
+
+struct DitWs {
+  float *phi, *h1, *temb, *mods, *nmod;
+  float *h_img, *h_txt;
+  void *tn;
+  BlockWs blk;
+  size_t bytes;
+};
+
+DitWs carve_dit(const lens_config *c, int B, int Si, int St, char *base) {
+  const size_t es = c->act_dtype == LENS_BF16 ? 2 : 4;
+  const size_t D = c->hidden;
+  DitWs w{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    void *p = base ? base + off : nullptr;
+    off += align_up(n);
+    return p;
+  };
+  w.phi = (float *)take((size_t)B * c->t_freq_dim * 4);
+  w.h1 = (float *)take((size_t)B * D * 4);
+  w.temb = (float *)take((size_t)B * D * 4);
+  w.mods = (float *)take((size_t)c->n_blocks * 2 * B * 6 * D * 4);
+  w.nmod = (float *)take((size_t)B * 2 * D * 4);
+  w.h_img = (float *)take((size_t)B * Si * D * 4);
+  w.h_txt = (float *)take((size_t)B * St * D * 4);
+  w.tn = take((size_t)B * St * c->txt_layers * c->txt_feat_dim * es);
+  w.blk = carve_block(c, B, Si, St, base ? base + off : nullptr, false);
+  off += w.blk.bytes;
+  w.bytes = off;
+  return w;
+}
+
+// ------------------------------------------------------------ launches
+lens_status gemm(lens_kernel_kind, int epi, bool bf, GemmProblem *p, int np, hipStream_t st) {
+  Timed t(LENS_KERNEL_GEMM, st);
+  hipError_t e = t.done(launch_gemm(epi, bf, p, np, st));
+  if (e != hipSuccess) return fail(LENS_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
+  return LENS_OK;
+}
+
+#define LTRY(expr)                   \
+  do {                               \
+    lens_status _s = (expr);         \
+    if (_s != LENS_OK) return _s;    \
+  } while (0)
+
+// The block after AdaLN: mod_img / mod_txt point at [B][6D] rows.
+lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img, float *h_txt, const float *mod_img,
+                       const float *mod_txt, const int32_t *img_pos, const int32_t *txt_pos, const int32_t *txt_len,
+                       int B, int Si, int St, const BlockWs &ws, hipStream_t st) {
+  const bool bf = c->act_dtype == LENS_BF16;
+  const int D = c->hidden, D6 = 6 * D;
+  const int Mi = B * Si, Mt = B * St;
+  hipError_t e;
+
+  // 1. pre-attention RMSNorm + modulation (shift1, scale1)
+  NormModProblem nm[2] = {
+      {h_img, ws.a_img, mod_img, mod_img + D, D6, Mi, Si > 0 ? Si : 1},
+      {h_txt, ws.a_txt, mod_txt, mod_txt + D, D6, Mt, St > 0 ? St : 1}};
+  {
+    Timed t(LENS_KERNEL_NORM, st);
+    e = t.done(launch_norm_modulate(nm, 2, D, c->eps, bf, st));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "norm launch failed: %s", hipGetErrorString(e));
+  }
+  // 2. QKV projections
+  GemmProblem g[2] = {};
+  g[0] = GemmProblem{ws.a_img, w->img.qkv.w, nullptr, w->img.qkv.b, nullptr, ws.qkv_img, nullptr, 0, 1, Mi, 3 * D, D};
+  g[1] = GemmProblem{ws.a_txt, w->txt.qkv.w, nullptr, w->txt.qkv.b, nullptr, ws.qkv_txt, nullptr, 0, 1, Mt, 3 * D, D};
+  LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE, bf, g, 2, st));
+  // 3. QK RMSNorm + RoPE -> joint Q, K, V^T
+  const int Sp = s_pad(Si, St);
+  QkRopeArgs qa{ws.qkv_img, ws.qkv_txt, w->img.q_gain, w->img.k_gain, w->txt.q_gain, w->txt.k_gain, img_pos, txt_pos,
+                ws.Q, ws.K, ws.Vt, B, c->heads, Si, St, Sp, c->rope_axes[0], c->rope_axes[1], c->rope_axes[2],
+                c->rope_theta, c->eps};
+  {
+    Timed t(LENS_KERNEL_QKNORM_ROPE, st);
+    e = t.done(launch_qknorm_rope(qa, bf, st));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "qk-norm/rope launch failed: %s", hipGetErrorString(e));
+  }
+  // 4. joint attention; outputs overwrite the (dead) norm outputs
+  AttnArgs aa{ws.Q, ws.K, ws.Vt, ws.a_img, ws.a_txt, txt_len, B, c->heads, Si, St, Sp, 0.125f};
+  {
+    Timed t(LENS_KERNEL_ATTENTION, st);
+    e = t.done(launch_attention(aa, bf, st));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  }
+  // 5. output projection + gated residual (gate1)
+  g[0] = GemmProblem{ws.a_img, w->img.out.w, nullptr, w->img.out.b, nullptr, h_img, mod_img + 2 * D, D6, Si > 0 ? Si : 1,
+                     Mi, D, D};
+  g[1] = GemmProblem{ws.a_txt, w->txt.out.w, nullptr, w->txt.out.b, nullptr, h_txt, mod_txt + 2 * D, D6, St > 0 ? St : 1,
+                     Mt, D, D};
+  LTRY(gemm(LENS_KERNEL_GEMM, EPI_GATED, bf, g, 2, st));
+  // 6. pre-MLP RMSNorm + modulation (shift2, scale2)
+  nm[0].shift = mod_img + 3 * D;
+  nm[0].scale = mod_img + 4 * D;
+  nm[1].shift = mod_txt + 3 * D;
+  nm[1].scale = mod_txt + 4 * D;
+  {
+    Timed t(LENS_KERNEL_NORM, st);
+    e = t.done(launch_norm_modulate(nm, 2, D, c->eps, bf, st));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "norm launch failed: %s", hipGetErrorString(e));
+  }
+  // 7. w1 | w3 with the SwiGLU epilogue (output reuses the qkv buffers)
+  const int F = c->mlp_hidden;
+  g[0] = GemmProblem{ws.a_img, w->img.w1.w, w->img.w3.w, w->img.w1.b, w->img.w3.b, ws.qkv_img, nullptr, 0, 1, Mi, F, D};
+  g[1] = GemmProblem{ws.a_txt, w->txt.w1.w, w->txt.w3.w, w->txt.w1.b, w->txt.w3.b, ws.qkv_txt, nullptr, 0, 1, Mt, F, D};
+  LTRY(gemm(LENS_KERNEL_GEMM, EPI_SWIGLU, bf, g, 2, st));
+  // 8. w2 + gated residual (gate2)
+  g[0] = GemmProblem{ws.qkv_img, w->img.w2.w, nullptr, w->img.w2.b, nullptr, h_img, mod_img + 5 * D, D6, Si > 0 ? Si : 1,
+                     Mi, D, F};
+  g[1] = GemmProblem{ws.qkv_txt, w->txt.w2.w, nullptr, w->txt.w2.b, nullptr, h_txt, mod_txt + 5 * D, D6, St > 0 ? St : 1,
+                     Mt, D, F};
+  LTRY(gemm(LENS_KERNEL_GEMM, EPI_GATED, bf, g, 2, st));
+  return LENS_OK;
+}
+
+lens_status adaln_all(const lens_config *c, const lens_block_w *const *blocks, int nblk, const float *temb, int B,
+                      float *mods, hipStream_t st) {
+  // mods: [nblk][2][B][6D]; problems in chunks of GEMV_MAX_PROBS
+  const bool bf = c->act_dtype == LENS_BF16;
+  const int D = c->hidden, D6 = 6 * D;
+  GemvBatch gb{};
+  auto flush = [&]() -> lens_status {
+    if (gb.nprob == 0) return LENS_OK;
+    Timed t(LENS_KERNEL_ADALN, st);
+    hipError_t e = t.done(launch_gemv(gb, temb, B, D, true, bf, st));
+    gb.nprob = 0;
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "AdaLN launch failed: %s", hipGetErrorString(e));
+    return LENS_OK;
+  };
+  for (int i = 0; i < nblk; ++i) {
+    for (int s = 0; s < 2; ++s) {
+      const lens_linear &l = s == 0 ? blocks[i]->img.mod : blocks[i]->txt.mod;
+      const int k = gb.nprob++;
+      gb.W[k] = l.w;
+      gb.bias[k] = l.b;
+      gb.y[k] = mods + ((size_t)i * 2 + s) * B * D6;
+      gb.N[k] = D6;
+      gb.y_stride[k] = D6;
+      if (gb.nprob == GEMV_MAX_PROBS) LTRY(flush());
+    }
+  }
+  return flush();
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+void lens_default_config(lens_config *c, lens_dtype act) {
+  if (!c) return;
+  c->hidden = 1536;
+  c->heads = 24;
+  c->head_dim = 64;
+  c->mlp_hidden = 4096;
+  c->n_blocks = 48;
+  c->rope_axes[0] = 8;
+  c->rope_axes[1] = 28;
+  c->rope_axes[2] = 28;
+  c->in_ch = 128;
+  c->out_ch = 128;
+  c->txt_feat_dim = 2880;
+  c->txt_layers = 4;
+  c->t_freq_dim = 256;
+  c->rope_theta = 10000.f;
+  c->eps = 1e-6f;
+  c->t_scale = 1000.f;
+  c->act_dtype = act;
+}
+
+size_t lens_block_workspace_bytes(const lens_config *c, int32_t B, int32_t Si, int32_t St) {
+  if (check_config(c) != LENS_OK || check_sizes(B, Si, St) != LENS_OK) return 0;
+  return carve_block(c, B, Si, St, nullptr, true).bytes;
+}
+
+size_t lens_dit_workspace_bytes(const lens_config *c, int32_t B, int32_t Si, int32_t St) {
+  if (check_dit_config(c) != LENS_OK || check_sizes(B, Si, St) != LENS_OK) return 0;
+  return carve_dit(c, B, Si, St, nullptr).bytes;
+}
+
+lens_status lens_block_forward(const lens_config *c, const lens_block_w *w, float *h_img, float *h_txt,
+                               const float *temb, const int32_t *img_pos, const int32_t *txt_pos,
+                               const int32_t *txt_len, int32_t B, int32_t Si, int32_t St, void *workspace,
+                               size_t ws_bytes, void *hip_stream) {
+  LTRY(check_config(c));
+  LTRY(check_sizes(B, Si, St));
+  LTRY(check_block_w(w, 0));
+  if (!h_img || !temb || !img_pos) return fail(LENS_ERR_INVALID_ARG, "h_img, temb and img_pos must not be NULL");
+  if (St > 0 && (!h_txt || !txt_pos)) return fail(LENS_ERR_INVALID_ARG, "h_txt and txt_pos must not be NULL");
+  const BlockWs need = carve_block(c, B, Si, St, nullptr, true);
+  if (!workspace || ws_bytes < need.bytes)
+    return fail(LENS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? ws_bytes : 0, need.bytes);
+  if ((uintptr_t)workspace % 256) return fail(LENS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)hip_stream;
+  const BlockWs ws = carve_block(c, B, Si, St, (char *)workspace, true);
+  const lens_block_w *bl[1] = {w};
+  LTRY(adaln_all(c, bl, 1, temb, B, ws.mod, st));
+  const float *mod_img = ws.mod, *mod_txt = ws.mod + (size_t)B * 6 * c->hidden;
+  return block_core(c, w, h_img, h_txt, mod_img, mod_txt, img_pos, txt_pos, txt_len, B, Si, St, ws, st);
+}
+
+lens_status lens_dit_forward(const lens_config *c, const lens_dit_w *w, const void *x, const void *txt_feats,
+                             const float *t, const int32_t *img_pos, const int32_t *txt_pos, const int32_t *txt_len,
+                             int32_t B, int32_t Si, int32_t St, float *v_out, void *workspace, size_t ws_bytes,
+                             void *hip_stream) {
+  LTRY(check_dit_config(c));
+  LTRY(check_sizes(B, Si, St));
+  if (!w) return fail(LENS_ERR_INVALID_ARG, "weight table is NULL");
+  LTRY(check_linear(w->t_fc1, "t_fc1"));
+  LTRY(check_linear(w->t_fc2, "t_fc2"));
+  LTRY(check_linear(w->img_in, "img_in"));
+  LTRY(check_linear(w->txt_in, "txt_in"));
+  LTRY(check_linear(w->norm_out, "norm_out"));
+  LTRY(check_linear(w->proj_out, "proj_out"));
+  if (!w->txt_gain) return fail(LENS_ERR_INVALID_ARG, "txt_gain is NULL");
+  if (c->n_blocks > 0 && !w->blocks) return fail(LENS_ERR_INVALID_ARG, "blocks is NULL");
+  for (int i = 0; i < c->n_blocks; ++i) LTRY(check_block_w(&w->blocks[i], i));
+  if (!x || !t || !img_pos || !v_out) return fail(LENS_ERR_INVALID_ARG, "x, t, img_pos and v_out must not be NULL");
+  if (St > 0 && (!txt_feats || !txt_pos))
+    return fail(LENS_ERR_INVALID_ARG, "txt_feats and txt_pos must not be NULL");
+  const DitWs need = carve_dit(c, B, Si, St, nullptr);
+  if (!workspace || ws_bytes < need.bytes)
+    return fail(LENS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? ws_bytes : 0, need.bytes);
+  if ((uintptr_t)workspace % 256) return fail(LENS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  const bool bf = c->act_dtype == LENS_BF16;
+  const DitWs ws = carve_dit(c, B, Si, St, (char *)workspace);
+  const int D = c->hidden;
+  hipError_t e;
+
+  // timestep embedding: phi(t) -> fc1 -> SiLU -> fc2
+  HIP_TRY(launch_timestep_features(t, ws.phi, B, c->t_freq_dim, c->t_scale, st));
+  {
+    GemvBatch gb{};
+    gb.nprob = 1;
+    gb.W[0] = w->t_fc1.w;
+    gb.bias[0] = w->t_fc1.b;
+    gb.y[0] = ws.h1;
+    gb.N[0] = D;
+    gb.y_stride[0] = D;
+    Timed tt(LENS_KERNEL_ADALN, st);
+    e = tt.done(launch_gemv(gb, ws.phi, B, c->t_freq_dim, false, bf, st));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "timestep fc1 failed: %s", hipGetErrorString(e));
+    gb.W[0] = w->t_fc2.w;
+    gb.bias[0] = w->t_fc2.b;
+    gb.y[0] = ws.temb;
+    Timed t2(LENS_KERNEL_ADALN, st);
+    e = t2.done(launch_gemv(gb, ws.h1, B, D, true, bf, st));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "timestep fc2 failed: %s", hipGetErrorString(e));
+  }
+  // AdaLN of every block (temb does not depend on the block) + norm_out
+  {
+    std::vector<const lens_block_w *> bl(c->n_blocks);
+    for (int i = 0; i < c->n_blocks; ++i) bl[i] = &w->blocks[i];
+    LTRY(adaln_all(c, bl.data(), c->n_blocks, ws.temb, B, ws.mods, st));
+    GemvBatch gb{};
+    gb.nprob = 1;
+    gb.W[0] = w->norm_out.w;
+    gb.bias[0] = w->norm_out.b;
+    gb.y[0] = ws.nmod;
+    gb.N[0] = 2 * D;
+    gb.y_stride[0] = 2 * D;
+    Timed tt(LENS_KERNEL_ADALN, st);
+    e = tt.done(launch_gemv(gb, ws.temb, B, D, true, bf, st));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "norm_out modulation failed: %s", hipGetErrorString(e));
+  }
+  // embeddings
+  GemmProblem g{x, w->img_in.w, nullptr, w->img_in.b, nullptr, ws.h_img, nullptr, 0, 1, B * Si, D, c->in_ch};
+  LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE_F32, bf, &g, 1, st));
+  if (St > 0) {
+    HIP_TRY(launch_txt_norm(txt_feats, w->txt_gain, ws.tn, B * St, c->txt_layers, c->txt_feat_dim, c->eps, bf, st));
+    g = GemmProblem{ws.tn, w->txt_in.w, nullptr, w->txt_in.b, nullptr, ws.h_txt, nullptr, 0, 1, B * St, D,
+                    c->txt_layers * c->txt_feat_dim};
+    LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE_F32, bf, &g, 1, st));
+  }
+  // blocks
+  for (int i = 0; i < c->n_blocks; ++i) {
+    const float *mi = ws.mods + (size_t)i * 2 * B * 6 * D;
+    const float *mt = mi + (size_t)B * 6 * D;
+    LTRY(block_core(c, &w->blocks[i], ws.h_img, ws.h_txt, mi, mt, img_pos, txt_pos, txt_len, B, Si, St, ws.blk, st));
+  }
+  // final layer
+  NormModProblem nm[1] = {{ws.h_img, ws.blk.a_img, ws.nmod, ws.nmod + D, 2 * D, B * Si, Si}};
+  {
+    Timed tt(LENS_KERNEL_NORM, st);
+    e = tt.done(launch_norm_modulate(nm, 1, D, c->eps, bf, st));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "norm_out launch failed: %s", hipGetErrorString(e));
+  }
+  g = GemmProblem{ws.blk.a_img, w->proj_out.w, nullptr, w->proj_out.b, nullptr, v_out, nullptr, 0, 1, B * Si,
+                  c->out_ch, D};
+  LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE_F32, bf, &g, 1, st));
+  return LENS_OK;
+}
+
+lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond, int64_t n, float dt,
+                           float cfg_scale, void *x_lowp_out, lens_dtype lowp_dtype, void *hip_stream) {
+  if (n < 0) return fail(LENS_ERR_INVALID_ARG, "n = %lld < 0", (long long)n);
+  if (n > 0 && (!x || !v_cond)) return fail(LENS_ERR_INVALID_ARG, "x and v_cond must not be NULL");
+  if (x_lowp_out && lowp_dtype != LENS_F32 && lowp_dtype != LENS_BF16)
+    return fail(LENS_ERR_INVALID_ARG, "lowp_dtype %d is not LENS_F32 or LENS_BF16", (int)lowp_dtype);
+  HIP_TRY(launch_flow_step(x, v_cond, v_uncond, n, dt, cfg_scale, x_lowp_out, lowp_dtype == LENS_BF16,
+                           (hipStream_t)hip_stream));
+  return LENS_OK;
+}
+
+lens_status lens_timer_start(lens_kernel_kind kind) {
+  if ((int)kind < 0 || (int)kind > (int)LENS_KERNEL_ADALN)
+    return fail(LENS_ERR_INVALID_ARG, "unknown kernel kind %d", (int)kind);
+  g_timer.kind = (int)kind;
+  g_timer.used = 0;
+  return LENS_OK;
+}
+
+lens_status lens_timer_stop(double *total_ms, int64_t *launches) {
+  double ms = 0.0;
+  const size_t n = g_timer.used / 2;
+  for (size_t i = 0; i < n; ++i) {
+    HIP_TRY(hipEventSynchronize(g_timer.pool[2 * i + 1]));
+    float f = 0.f;
+    HIP_TRY(hipEventElapsedTime(&f, g_timer.pool[2 * i], g_timer.pool[2 * i + 1]));
+    ms += f;
+  }
+  g_timer.kind = -1;
+  g_timer.used = 0;
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = (int64_t)n;
+  return LENS_OK;
+}
+
+const char *lens_status_string(lens_status s) {
+  switch (s) {
+    case LENS_OK: return "LENS_OK";
+    case LENS_ERR_INVALID_ARG: return "LENS_ERR_INVALID_ARG";
+    case LENS_ERR_UNSUPPORTED: return "LENS_ERR_UNSUPPORTED";
+    case LENS_ERR_WORKSPACE: return "LENS_ERR_WORKSPACE";
+    case LENS_ERR_HIP: return "LENS_ERR_HIP";
+  }
+  return "unknown lens_status";
+}
+
+const char *lens_last_error(void) { return g_err.c_str(); }
+
+const char *lens_version(void) { return "lens-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

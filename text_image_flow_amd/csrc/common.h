@@ -1,0 +1,117 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lens {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16-byte staging
+
+// float <-> bf16 with round-to-nearest-even (NaN stays NaN).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `stream` and return hipSuccess or the launch error.
+
+enum Epilogue {
+  EPI_STORE = 0,     // C = acc + bias                    (C in act type)
+  EPI_STORE_F32 = 1, // C = acc + bias                    (C float)
+  EPI_GATED = 2,     // H += gate[m / rows_per_gate] * (acc + bias)   (H float)
+  EPI_SWIGLU = 3     // C = silu(acc1 + b1) * (acc3 + b3), B rows from w1 and w3
+};
+
+// One GEMM problem: C[M, N] = A[M, K] . W[N, K]^T (+ epilogue).
+struct GemmProblem {
+  const void *A;       // [M, K] act type
+  const void *W;       // [N, K] act type (for SWIGLU: w1)
+  const void *W3;      // SWIGLU only: w3 [N, K]
+  const void *bias;    // [N] or NULL (SWIGLU: b1)
+  const void *bias3;   // SWIGLU only: b3 or NULL
+  void *C;             // output (see Epilogue)
+  const float *gate;   // EPI_GATED: gate rows, gate[(m / rows_per_gate) * gate_stride + n]
+  int64_t gate_stride;
+  int32_t rows_per_gate;
+  int32_t M, N, K;
+};
+
+// Grouped launch of up to 2 problems that share N, K and the epilogue.
+hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream);
+
+// Joint attention.  Q, K: [B, H, S_pad, 64]; Vt: [B, H, 64, S_pad] (act type).
+// Output rows p < S_img go to O_img[(b*S_img + p), h*64 + d], rows
+// S_img <= p < S_img + S_txt to O_txt[(b*S_txt + p - S_img), ...].
+// Valid keys of sample b: [0, S_img + clamp(txt_len[b], 0, S_txt)).
+struct AttnArgs {
+  const void *Q, *K, *Vt;
+  void *O_img, *O_txt;
+  const int32_t *txt_len;  // device, [B] or NULL
+  int32_t B, H, S_img, S_txt, S_pad;
+  float scale;             // 1/sqrt(head_dim)
+};
+hipError_t launch_attention(const AttnArgs &a, bool bf16_path, hipStream_t stream);
+
+// Per-row RMSNorm (no gain) + modulation, both streams in one launch.
+// out[r] = h[r] / rms(h[r]) * (1 + scale[b]) + shift[b], b = r / rows_per_sample.
+struct NormModProblem {
+  const float *h;
+  void *out;
+  const float *shift, *scale;  // [B, D] rows, stride mod_stride
+  int64_t mod_stride;
+  int32_t rows, rows_per_sample;
+};
+hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float eps, bool bf16_path,
+                                hipStream_t stream);
+
+// QK RMSNorm + RoPE + joint layout.  qkv_img [B*S_img, 3D], qkv_txt [B*S_txt, 3D].
+struct QkRopeArgs {
+  const void *qkv_img, *qkv_txt;
+  const void *qg_img, *kg_img, *qg_txt, *kg_txt;  // [64] act type
+  const int32_t *pos_img, *pos_txt;               // [S, 3]
+  void *Q, *K, *Vt;
+  int32_t B, H, S_img, S_txt, S_pad;
+  int32_t axes0, axes1, axes2;
+  float theta, eps;
+};
+hipError_t launch_qknorm_rope(const QkRopeArgs &a, bool bf16_path, hipStream_t stream);
+
+// Skinny GEMM (GEMV over a small batch): y[b, n] = sum_k f(x[b, k]) W[n, k] + bias[n],
+// f = SiLU when silu_in, else identity.  x float [B, K], y float [B, N] rows at
+// y + b * y_stride.  Up to GEMV_MAX_PROBS problems share x, B and K.
+constexpr int GEMV_MAX_PROBS = 24;
+struct GemvBatch {
+  const void *W[GEMV_MAX_PROBS];
+  const void *bias[GEMV_MAX_PROBS];
+  float *y[GEMV_MAX_PROBS];
+  int32_t N[GEMV_MAX_PROBS];
+  int64_t y_stride[GEMV_MAX_PROBS];
+  int32_t nprob;
+};
+hipError_t launch_gemv(const GemvBatch &g, const float *x, int B, int K, bool silu_in, bool bf16_path,
+                       hipStream_t stream);
+
+// Sinusoidal timestep features: phi[b] = [cos(scale t w_k) | sin(scale t w_k)].
+hipError_t launch_timestep_features(const float *t, float *phi, int B, int dim, float t_scale,
+                                    hipStream_t stream);
+
+// Text input: per encoder layer RMSNorm with gain; rows of layers * F.
+hipError_t launch_txt_norm(const void *feats, const void *gain, void *out, int rows, int layers, int F,
+                           float eps, bool bf16_path, hipStream_t stream);
+
+// Euler + CFG step on n elements.
+hipError_t launch_flow_step(float *x, const float *vc, const float *vu, int64_t n, float dt, float s,
+                            void *lowp, int lowp_bf16, hipStream_t stream);
+
+}  // namespace lens

@@ -1,0 +1,400 @@
+// Bandwidth-bound kernels of the denoiser step:
+//   * RMSNorm + AdaLN modulation (Lens-Turbo-3.8B-bf16 article, "自适应调制与
+//     RMSNorm"; shift/scale/gate order from the Lens blog's "Overview");
+//   * per-head QK RMSNorm + 3-axis RoPE, writing the joint attention layout
+//     (same article: norm_q/norm_k/norm_added_q/norm_added_k; "3D RoPE",
+//     axes [8, 28, 28]);
+//   * the skinny GEMM of AdaLN and the timestep MLP (time_text_embed);
+//   * timestep sinusoid; per-layer text-feature RMSNorm (txt_norm.0..3);
+//   * the CFG + Euler flow step (SOTA image-generation survey, "CFG" and
+//     "Rectified Flow"; the flow-matching path of the Lens paper summary).
+// Statistics and arithmetic are float32; stores round to the storage type.
+#include "common.h"
+
+namespace lens {
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T *dst, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float *dst, float a, float b, float c, float d) {
+  *(float4 *)dst = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16 *dst, float a, float b, float c, float d) {
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *(bf16x4 *)dst = v;
+}
+
+// ------------------------------------------------ RMSNorm + modulation
+// One wave per row; D % 256 == 0 so each lane owns D/256 float4 groups.
+template <typename T, int G>
+__global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, NormModProblem p1, float eps) {
+  constexpr int D = G * 256;
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const bool second = row >= p0.rows;
+  const NormModProblem p = second ? p1 : p0;
+  if (second) {
+    row -= p0.rows;
+    if (row >= p1.rows) return;
+  }
+  const float *x = p.h + (int64_t)row * D;
+  const int b = row / p.rows_per_sample;
+  const float *sh = p.shift + (int64_t)b * p.mod_stride;
+  const float *sc = p.scale + (int64_t)b * p.mod_stride;
+  float4 v[G];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    v[i] = *(const float4 *)(x + (i * 64 + lane) * 4);
+    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  }
+  ss = wave_sum(ss);
+  const float r = rsqrtf(ss / (float)D + eps);
+  T *out = (T *)p.out + (int64_t)row * D;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int c = (i * 64 + lane) * 4;
+    const float4 s4 = *(const float4 *)(sc + c), h4 = *(const float4 *)(sh + c);
+    store4<T>(out + c, v[i].x * r * (1.f + s4.x) + h4.x, v[i].y * r * (1.f + s4.y) + h4.y,
+              v[i].z * r * (1.f + s4.z) + h4.z, v[i].w * r * (1.f + s4.w) + h4.w);
+  }
+}
+
+// ------------------------------------------------ QK RMSNorm + RoPE
+// Block = 64 joint positions x one head; thread t: position t/4, dims
+// [(t%4)*16, +16).  V is transposed through LDS so V^T rows are written as
+// contiguous 128-byte runs.
+template <typename T>
+__device__ __forceinline__ void load16(const T *src, float *v) {
+  for (int i = 0; i < 16; ++i) v[i] = to_f32(src[i]);
+}
+template <>
+__device__ __forceinline__ void load16<bf16>(const bf16 *src, float *v) {
+  const bf16x8 a = *(const bf16x8 *)src, b = *(const bf16x8 *)(src + 8);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = (float)a[i];
+    v[8 + i] = (float)b[i];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store16(T *dst, const float *v) {
+  for (int i = 0; i < 16; ++i) dst[i] = from_f32<T>(v[i]);
+}
+template <>
+__device__ __forceinline__ void store16<bf16>(bf16 *dst, const float *v) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (bf16)v[i];
+    b[i] = (bf16)v[8 + i];
+  }
+  *(bf16x8 *)dst = a;
+  *(bf16x8 *)(dst + 8) = b;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
+  __shared__ float sV[64][64 + 1];
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int t = threadIdx.x, tok = t >> 2, qd = t & 3, d0 = qd * 16;
+  const int p = blockIdx.x * 64 + tok;
+  const int S = a.S_img + a.S_txt;
+  const int D = a.H * 64;
+  const int64_t bh = (int64_t)b * a.H + h;
+  T *Qo = (T *)a.Q + (bh * a.S_pad + p) * 64 + d0;
+  T *Ko = (T *)a.K + (bh * a.S_pad + p) * 64 + d0;
+
+  float q[16], k[16], v[16];
+  bool live = p < S;
+  const T *src = nullptr;
+  const T *qg = nullptr, *kg = nullptr;
+  const int32_t *pos = nullptr;
+  if (p < a.S_img) {
+    src = (const T *)a.qkv_img + ((int64_t)b * a.S_img + p) * 3 * D;
+    qg = (const T *)a.qg_img;
+    kg = (const T *)a.kg_img;
+    pos = a.pos_img + 3 * p;
+  } else if (live) {
+    src = (const T *)a.qkv_txt + ((int64_t)b * a.S_txt + (p - a.S_img)) * 3 * D;
+    qg = (const T *)a.qg_txt;
+    kg = (const T *)a.kg_txt;
+    pos = a.pos_txt + 3 * (p - a.S_img);
+  }
+  if (live) {
+    load16<T>(src + h * 64 + d0, q);
+    load16<T>(src + D + h * 64 + d0, k);
+    load16<T>(src + 2 * D + h * 64 + d0, v);
+  } else {
+    for (int i = 0; i < 16; ++i) q[i] = k[i] = v[i] = 0.f;
+  }
+  float sq = 0.f, sk = 0.f;
+  for (int i = 0; i < 16; ++i) {
+    sq += q[i] * q[i];
+    sk += k[i] * k[i];
+  }
+  // the four threads of a position are lanes 4j..4j+3 of one wave
+  sq += __shfl_xor(sq, 1);
+  sq += __shfl_xor(sq, 2);
+  sk += __shfl_xor(sk, 1);
+  sk += __shfl_xor(sk, 2);
+  if (live) {
+    const float rq = rsqrtf(sq / 64.f + a.eps), rk = rsqrtf(sk / 64.f + a.eps);
+    const float p0 = (float)pos[0], p1 = (float)pos[1], p2 = (float)pos[2];
+    const float l2t = log2f(a.theta);
+    for (int i = 0; i < 16; i += 2) {
+      const int d = d0 + i;
+      // axis segment and pair index inside it
+      float pa, j, w;
+      if (d < a.axes0) {
+        pa = p0; j = (float)(d / 2); w = (float)a.axes0;
+      } else if (d < a.axes0 + a.axes1) {
+        pa = p1; j = (float)((d - a.axes0) / 2); w = (float)a.axes1;
+      } else {
+        pa = p2; j = (float)((d - a.axes0 - a.axes1) / 2); w = (float)a.axes2;
+      }
+      const float ang = pa * exp2f(-2.f * j / w * l2t);
+      float sn, cs;
+      sincosf(ang, &sn, &cs);
+      const float q0 = q[i] * rq * to_f32(qg[d]), q1 = q[i + 1] * rq * to_f32(qg[d + 1]);
+      const float k0 = k[i] * rk * to_f32(kg[d]), k1 = k[i + 1] * rk * to_f32(kg[d + 1]);
+      q[i] = q0 * cs - q1 * sn;
+      q[i + 1] = q0 * sn + q1 * cs;
+      k[i] = k0 * cs - k1 * sn;
+      k[i + 1] = k0 * sn + k1 * cs;
+    }
+  }
+  store16<T>(Qo, q);
+  store16<T>(Ko, k);
+  for (int i = 0; i < 16; ++i) sV[d0 + i][tok] = v[i];
+  __syncthreads();
+  // V^T [d][p]: thread t writes d = t/4, positions (t%4)*16 .. +16
+  {
+    const int d = t >> 2, c0 = (t & 3) * 16;
+    float tmp[16];
+    for (int i = 0; i < 16; ++i) tmp[i] = sV[d][c0 + i];
+    store16<T>((T *)a.Vt + (bh * 64 + d) * a.S_pad + blockIdx.x * 64 + c0, tmp);
+  }
+}
+
+// ------------------------------------------------ skinny GEMM (GEMV)
+// y[b, n] = sum_k f(x[b, k]) W[n, k] + bias[n] for b < B (B <= 8 per launch).
+// One wave per output row n, 8 rows per wave; f(x) staged in LDS once.
+constexpr int GEMV_ROWS_PER_WAVE = 8;
+constexpr int GEMV_MAXB = 8;
+
+template <typename T, int NB>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvBatch g, const float *x, int K, int silu_in) {
+  extern __shared__ float sx[];  // [NB][K]
+  const int prob = blockIdx.y;
+  const int N = g.N[prob];
+  const int nbase = blockIdx.x * 4 * GEMV_ROWS_PER_WAVE;
+  if (nbase >= N) return;
+  for (int e = threadIdx.x; e < NB * K; e += 256) {
+    const float v = x[e];
+    sx[e] = silu_in ? silu_f(v) : v;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const T *W = (const T *)g.W[prob];
+  const T *bias = (const T *)g.bias[prob];
+  for (int rr = 0; rr < GEMV_ROWS_PER_WAVE; ++rr) {
+    const int n = nbase + wave * GEMV_ROWS_PER_WAVE + rr;
+    if (n >= N) break;
+    const T *wr = W + (int64_t)n * K;
+    float acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+    for (int k = lane * 8; k < K; k += 512) {
+      float w[8];
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 wv = *(const bf16x8 *)(wr + k);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = (float)wv[i];
+      } else {
+        const float4 a = *(const float4 *)(wr + k), c = *(const float4 *)(wr + k + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float *xb = sx + b * K + k;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[b] = fmaf(w[i], xb[i], acc[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = wave_sum(acc[b]);
+    if (lane == 0) {
+      const float bv = bias ? to_f32(bias[n]) : 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) g.y[prob][(int64_t)b * g.y_stride[prob] + n] = acc[b] + bv;
+    }
+  }
+}
+
+template <typename T, int NB>
+hipError_t gemv_run(const GemvBatch &g, const float *x, int K, bool silu_in, hipStream_t st) {
+  int maxN = 0;
+  for (int i = 0; i < g.nprob; ++i) maxN = g.N[i] > maxN ? g.N[i] : maxN;
+  const int rows_per_block = 4 * GEMV_ROWS_PER_WAVE;
+  dim3 grid((maxN + rows_per_block - 1) / rows_per_block, g.nprob);
+  hipLaunchKernelGGL((gemv_kernel<T, NB>), grid, dim3(256), NB * K * sizeof(float), st, g, x, K, silu_in ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t gemv_dispatch(const GemvBatch &g, const float *x, int B, int K, bool silu_in, hipStream_t st) {
+  // batches larger than 8 run as several launches on row offsets of x / y
+  for (int b0 = 0; b0 < B; b0 += GEMV_MAXB) {
+    const int nb = B - b0 < GEMV_MAXB ? B - b0 : GEMV_MAXB;
+    GemvBatch gg = g;
+    for (int i = 0; i < g.nprob; ++i) gg.y[i] = g.y[i] + (int64_t)b0 * g.y_stride[i];
+    const float *xx = x + (int64_t)b0 * K;
+    hipError_t e;
+    switch (nb) {
+      case 1: e = gemv_run<T, 1>(gg, xx, K, silu_in, st); break;
+      case 2: e = gemv_run<T, 2>(gg, xx, K, silu_in, st); break;
+      case 3: e = gemv_run<T, 3>(gg, xx, K, silu_in, st); break;
+      case 4: e = gemv_run<T, 4>(gg, xx, K, silu_in, st); break;
+      case 5: e = gemv_run<T, 5>(gg, xx, K, silu_in, st); break;
+      case 6: e = gemv_run<T, 6>(gg, xx, K, silu_in, st); break;
+      case 7: e = gemv_run<T, 7>(gg, xx, K, silu_in, st); break;
+      default: e = gemv_run<T, 8>(gg, xx, K, silu_in, st); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ------------------------------------------------ timestep features
+__global__ void timestep_kernel(const float *t, float *phi, int B, int dim, float t_scale) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = dim / 2;
+  if (i >= B * half) return;
+  const int b = i / half, k = i % half;
+  // w_k = 10000^(-k/half), computed in double so the phase of t_scale * t
+  // (up to 1000 rad) keeps full float accuracy
+  const double w = exp(-(double)k / (double)half * log(10000.0));
+  const double arg = (double)t_scale * (double)t[b] * w;
+  phi[(int64_t)b * dim + k] = (float)cos(arg);
+  phi[(int64_t)b * dim + half + k] = (float)sin(arg);
+}
+
+// ------------------------------------------------ text feature RMSNorm
+// One block per token row; wave w normalises layers w, w+4, ...
+template <typename T>
+__global__ __launch_bounds__(256) void txt_norm_kernel(const T *feats, const T *gain, T *out, int layers, int F,
+                                                       float eps) {
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int l = wave; l < layers; l += 4) {
+    const T *x = feats + ((int64_t)row * layers + l) * F;
+    T *y = out + ((int64_t)row * layers + l) * F;
+    float ss = 0.f;
+    for (int i = lane; i < F; i += 64) {
+      const float v = to_f32(x[i]);
+      ss += v * v;
+    }
+    ss = wave_sum(ss);
+    const float r = rsqrtf(ss / (float)F + eps);
+    for (int i = lane; i < F; i += 64) y[i] = from_f32<T>(to_f32(x[i]) * r * to_f32(gain[(int64_t)l * F + i]));
+  }
+}
+
+// ------------------------------------------------ CFG + Euler
+template <typename TL>
+__global__ void flow_step_kernel(float *x, const float *vc, const float *vu, int64_t n, float dt, float s,
+                                 TL *lowp) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float c = vc[i];
+    const float v = vu ? vu[i] + s * (c - vu[i]) : c;
+    const float xn = x[i] + dt * v;
+    x[i] = xn;
+    if (lowp) lowp[i] = from_f32<TL>(xn);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float eps, bool bf16_path,
+                                hipStream_t stream) {
+  NormModProblem p1 = nprob > 1 ? p[1] : NormModProblem{};
+  if (nprob < 2) p1.rows = 0;
+  const int rows = p[0].rows + p1.rows;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((rows + 3) / 4);
+#define NORM_CASE(g)                                                                                     \
+  case g:                                                                                                \
+    if (bf16_path)                                                                                       \
+      hipLaunchKernelGGL((norm_modulate_kernel<bf16, g>), grid, dim3(256), 0, stream, p[0], p1, eps);   \
+    else                                                                                                 \
+      hipLaunchKernelGGL((norm_modulate_kernel<float, g>), grid, dim3(256), 0, stream, p[0], p1, eps);  \
+    break;
+  switch (D / 256) {
+    NORM_CASE(1) NORM_CASE(2) NORM_CASE(3) NORM_CASE(4) NORM_CASE(5) NORM_CASE(6) NORM_CASE(7) NORM_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef NORM_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_qknorm_rope(const QkRopeArgs &a, bool bf16_path, hipStream_t stream) {
+  dim3 grid(a.S_pad / 64, a.H, a.B);
+  if (bf16_path)
+    hipLaunchKernelGGL(qknorm_rope_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(qknorm_rope_kernel<float>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const GemvBatch &g, const float *x, int B, int K, bool silu_in, bool bf16_path,
+                       hipStream_t stream) {
+  if (g.nprob == 0 || B == 0) return hipSuccess;
+  return bf16_path ? gemv_dispatch<bf16>(g, x, B, K, silu_in, stream)
+                   : gemv_dispatch<float>(g, x, B, K, silu_in, stream);
+}
+
+hipError_t launch_timestep_features(const float *t, float *phi, int B, int dim, float t_scale,
+                                    hipStream_t stream) {
+  const int n = B * (dim / 2);
+  hipLaunchKernelGGL(timestep_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, t, phi, B, dim, t_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_txt_norm(const void *feats, const void *gain, void *out, int rows, int layers, int F, float eps,
+                           bool bf16_path, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (bf16_path)
+    hipLaunchKernelGGL(txt_norm_kernel<bf16>, dim3(rows), dim3(256), 0, stream, (const bf16 *)feats,
+                       (const bf16 *)gain, (bf16 *)out, layers, F, eps);
+  else
+    hipLaunchKernelGGL(txt_norm_kernel<float>, dim3(rows), dim3(256), 0, stream, (const float *)feats,
+                       (const float *)gain, (float *)out, layers, F, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_flow_step(float *x, const float *vc, const float *vu, int64_t n, float dt, float s, void *lowp,
+                            int lowp_bf16, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (lowp_bf16)
+    hipLaunchKernelGGL(flow_step_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, vc, vu, n, dt, s,
+                       (bf16 *)lowp);
+  else
+    hipLaunchKernelGGL(flow_step_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, x, vc, vu, n, dt, s,
+                       (float *)lowp);
+  return hipGetLastError();
+}
+
+}  // namespace lens
