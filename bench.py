@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Throughput of one classifier-free-guided denoising step of the 48-block
+Lens MM-DiT at 1024x1024 (64 x 64 = 4096 image tokens + 512 text tokens) on
+one MI355X.
+
+A step is the whole hot path: lens_dit_forward on a batch of 2 (cond and
+uncond samples sharing x and t: timestep MLP, AdaLN of all blocks, img_in,
+txt_norm + txt_in, 48 double-stream blocks, norm_out + proj_out) followed by
+lens_flow_step (CFG 5.0 combine + Euler update + bf16 copy of x for the next
+forward).  Weights are random-init bf16 (N(0, 0.02)), inputs are seeded
+synthetic tensors of the real shapes, and everything is resident in HBM
+before the timed region starts.
+
+Prints one JSON line.  `value` is achieved TFLOP/s over the whole step
+(algorithmic FLOPs: 2 M N K per GEMM, 4 S_q S_kv d H for attention over
+valid keys).  A second timed region records HIP events around every kernel
+launch (the library's opt-in timer) for the per-family breakdown and the
+roofline of the dominant kernel family.  `cpu_baseline` times the fp64
+oracle on a bounded sample (one block at the same shape) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+
+S_IMG, S_TXT, GRID = 4096, 512, (64, 64)
+CFG_SCALE = 5.0
+LOOP_STEPS = 20
+
+
+def block_flops(d, S_img, S_txt, B, q_valid=None, kv_valid=None):
+    """Algorithmic FLOPs of one block for B samples (AdaLN included)."""
+    D, F, H = d.hidden, d.mlp, d.heads
+    gemm = 0
+    for S in (S_img, S_txt):
+        gemm += 2 * B * S * D * (3 * D + D + 2 * F) + 2 * B * S * F * D
+    adaln = 2 * 2 * B * D * 6 * D
+    Sq = S_img + S_txt if q_valid is None else q_valid
+    Skv = S_img + S_txt if kv_valid is None else kv_valid
+    attn = 4 * B * Sq * Skv * d.head_dim * H
+    return gemm, attn, adaln
+
+
+def step_flops(d, S_img, S_txt, B):
+    g, a, m = block_flops(d, S_img, S_txt, B)
+    D = d.hidden
+    emb = 2 * B * (S_img * d.in_ch * D + S_txt * d.txt_layers * d.txt_feat * D + S_img * D * d.out_ch)
+    tmlp = 2 * B * (d.t_freq * D + D * D + D * 2 * D)
+    return {"gemm_blocks": d.n_blocks * g, "attention": d.n_blocks * a, "adaln": d.n_blocks * m,
+            "gemm_embed": emb, "small": tmlp,
+            "total": d.n_blocks * (g + a + m) + emb + tmlp}
+
+
+def cpu_baseline(d):
+    """The oracle as it stands, on one block at 1024^2 (B = 1), fp64."""
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = synth.block_weights(0, dtype="bf16")
+    hi, ht, temb = synth.block_inputs(1, S_IMG, S_TXT, dtype="bf16")
+    ip, tp = synth.image_positions(*GRID), synth.text_positions(S_TXT)
+    t0 = time.perf_counter()
+    O.block_forward(w, hi, ht, temb, ip, tp, None)
+    dt = time.perf_counter() - t0
+    g, a, m = block_flops(d, S_IMG, S_TXT, 1)
+    return {"value": round((g + a + m) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"oracle.block_forward: one block at 1024^2 (4096 image + 512 text tokens), B=1, fp64 numpy, "
+                      f"{dt:.2f} s for {(g + a + m) / 1e9:.1f} GFLOP; host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timer", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the path has no multi-GPU part (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import text_image_flow_amd as T
+    from text_image_flow_amd import _lib as L
+    from text_image_flow_amd import device as dv
+
+    dv.require_gpu()
+    torch.cuda.set_device(0)
+    d = synth.LENS
+    cfg = T.default_config(T.LENS_BF16)
+    B = 2
+
+    # ---- weights and inputs, resident in HBM before timing
+    t_setup = time.perf_counter()
+    top = synth.top_weights(d)
+    blocks = [dv.DeviceBlock(w, T.LENS_BF16) for _, w in synth.all_block_weights(d, threads=16)]
+    dit = dv.DeviceDit(top, blocks, T.LENS_BF16)
+    x0 = synth.latents(1, S_IMG, d)
+    x = dv.upload(x0)                                                   # f32 latent tokens [1, S, 128]
+    x_act = dv.upload(np.concatenate([synth.bf16_round(x0)] * B), T.LENS_BF16)
+    feats = dv.upload(np.concatenate([synth.text_features(1, S_TXT, d, seed=synth.SEED_TEXT_COND),
+                                      synth.text_features(1, S_TXT, d, seed=synth.SEED_TEXT_UNCOND)]), T.LENS_BF16)
+    ip, tp = dv.upload(synth.image_positions(*GRID)), dv.upload(synth.text_positions(S_TXT))
+    ts = dv.time_grid(LOOP_STEPS)
+    t_tab = dv.upload(np.repeat(ts[:, None], B, axis=1))
+    v = torch.empty((B, S_IMG, d.out_ch), dtype=torch.float32, device="cuda")
+    ws = dv.Workspace()
+    ws.get(T.lens_dit_workspace_bytes(cfg, B, S_IMG, S_TXT))
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    k_state = [0]
+
+    def step():
+        k = k_state[0] % LOOP_STEPS
+        k_state[0] += 1
+        dv.dit_forward(cfg, dit, x_act, feats, t_tab[k], ip, tp, None, v, ws)
+        dv.flow_step(x, v[:1], v[1:], float(ts[k + 1] - ts[k]), CFG_SCALE, x_act[:1], T.LENS_BF16)
+        x_act[1:].copy_(x_act[:1])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(v).all().item() and torch.isfinite(x).all().item(), "non-finite output"
+
+    fl = step_flops(d, S_IMG, S_TXT, B)
+    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
+
+    # ---- second timed region: per-family kernel timing with HIP events
+    kernels, roof = {}, None
+    if not args.no_kernel_timer:
+        L.check(T.lens_timer_start((1 << L.LENS_KERNEL_COUNT) - 1))
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        st, ms, n = T.lens_timer_stop()
+        L.check(st)
+        fam_flops = {"gemm": fl["gemm_blocks"] + fl["gemm_embed"], "attention": fl["attention"],
+                     "adaln": fl["adaln"] + fl["small"]}
+        for i, name in enumerate(L.KERNEL_NAMES):
+            if n[i] == 0:
+                continue
+            e = {"ms_per_step": round(ms[i] / args.steps, 4), "launches_per_step": n[i] // args.steps,
+                 "avg_launch_us": round(1e3 * ms[i] / n[i], 2)}
+            if name in fam_flops:
+                e["TFLOP/s"] = round(fam_flops[name] / (ms[i] / args.steps * 1e-3) / 1e12, 1)
+            kernels[name] = e
+        dom = max(("gemm", "attention"), key=lambda k: kernels.get(k, {}).get("ms_per_step", 0))
+        i = L.KERNEL_NAMES.index(dom)
+        per_launch_flops = fam_flops[dom] / (n[i] / args.steps)
+        avg_s = ms[i] / n[i] * 1e-3
+        ach = per_launch_flops / avg_s / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": per_launch_flops, "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(d)
+
+    out = {
+        "metric": "ms & TFLOP/s per 48-block DiT step at 1024^2 (4096+512 tok), % bf16 MFMA peak",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Lens MM-DiT CFG denoising step, 1024x1024", "image_tokens": S_IMG,
+                   "text_tokens": S_TXT, "batch": B, "cfg": "cond+uncond in one batch, scale 5.0",
+                   "blocks": d.n_blocks, "hidden": d.hidden, "heads": d.heads, "mlp": d.mlp,
+                   "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "flops_per_step": fl["total"], "wall_s": round(wall, 3), "setup_s": round(setup_s, 1),
+        "kernels": kernels, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -173,22 +173,25 @@ lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond,
                            float cfg_scale, void *x_lowp_out, lens_dtype lowp_dtype, void *hip_stream);
 
 /*
- * Opt-in kernel timer for measurement.  lens_timer_start(kind) makes every
- * later launch of that kernel family (see lens_kernel_kind) on any stream
- * record HIP events around itself; lens_timer_stop() synchronises those
- * events, returns the summed kernel milliseconds and the launch count, and
- * switches the timer off.  Not thread-safe; meant for a single benchmark
- * thread.
+ * Opt-in kernel timer for measurement.  lens_timer_start(mask) makes every
+ * later launch of the kernel families whose bit (1 << lens_kernel_kind) is
+ * set record a pair of HIP events around itself, on the stream it is
+ * launched on.  lens_timer_stop(ms, launches) synchronises those events,
+ * writes the summed kernel milliseconds and launch counts per family into
+ * ms[LENS_KERNEL_COUNT] and launches[LENS_KERNEL_COUNT] (either may be
+ * NULL), and switches the timer off.  Not thread-safe; meant for one
+ * benchmark thread.
  */
 typedef enum {
-  LENS_KERNEL_GEMM = 0,      /* bf16 MFMA GEMM (all projections) */
-  LENS_KERNEL_ATTENTION = 1, /* joint flash attention */
-  LENS_KERNEL_NORM = 2,      /* RMSNorm + modulation */
-  LENS_KERNEL_QKNORM_ROPE = 3,
-  LENS_KERNEL_ADALN = 4      /* skinny GEMV (AdaLN, timestep MLP) */
+  LENS_KERNEL_GEMM = 0,        /* bf16 MFMA GEMM (all projections) */
+  LENS_KERNEL_ATTENTION = 1,   /* joint flash attention */
+  LENS_KERNEL_NORM = 2,        /* RMSNorm + modulation */
+  LENS_KERNEL_QKNORM_ROPE = 3, /* QK RMSNorm + RoPE + joint layout */
+  LENS_KERNEL_ADALN = 4,       /* skinny GEMV (AdaLN, timestep MLP) */
+  LENS_KERNEL_COUNT = 5
 } lens_kernel_kind;
-lens_status lens_timer_start(lens_kernel_kind kind);
-lens_status lens_timer_stop(double *total_ms, int64_t *launches);
+lens_status lens_timer_start(uint32_t kind_mask);
+lens_status lens_timer_stop(double *ms, int64_t *launches);
 
 const char *lens_status_string(lens_status s);
 const char *lens_last_error(void);

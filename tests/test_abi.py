@@ -122,6 +122,7 @@ def test_dit_and_flow_argument_checks():
 
 
 def test_timer_argument_check():
-    assert T.lens_timer_start(99) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_timer_start(1 << 7) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_timer_start(0b11) == L.LENS_OK
     st, ms, n = T.lens_timer_stop()
-    assert st == L.LENS_OK and n == 0 and ms == 0.0
+    assert st == L.LENS_OK and n == [0] * 5 and ms == [0.0] * 5

@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(_HERE, "liblens.so")
 LENS_OK, LENS_ERR_INVALID_ARG, LENS_ERR_UNSUPPORTED, LENS_ERR_WORKSPACE, LENS_ERR_HIP = 0, -1, -2, -3, -4
 LENS_F32, LENS_BF16 = 0, 1
 LENS_KERNEL_GEMM, LENS_KERNEL_ATTENTION, LENS_KERNEL_NORM, LENS_KERNEL_QKNORM_ROPE, LENS_KERNEL_ADALN = range(5)
+LENS_KERNEL_COUNT = 5
+KERNEL_NAMES = ("gemm", "attention", "norm", "qknorm_rope", "adaln")
 
 # every function lens.h declares (checked against the header by the tests)
 EXPORTS = (
@@ -74,7 +76,7 @@ def lib() -> C.CDLL:
             "lens_block_forward": (C.c_int, [cfgp, C.POINTER(LensBlockW), P, P, P, P, P, P, I32, I32, I32, P, SZ, P]),
             "lens_dit_forward": (C.c_int, [cfgp, C.POINTER(LensDitW), P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]),
             "lens_flow_step": (C.c_int, [P, P, P, I64, F, F, P, C.c_int, P]),
-            "lens_timer_start": (C.c_int, [C.c_int]),
+            "lens_timer_start": (C.c_int, [C.c_uint32]),
             "lens_timer_stop": (C.c_int, [C.POINTER(D), C.POINTER(I64)]),
             "lens_status_string": (C.c_char_p, [C.c_int]),
             "lens_last_error": (C.c_char_p, []),
@@ -135,11 +137,12 @@ def lens_flow_step(x, v_cond, v_uncond, n, dt, cfg_scale, x_lowp_out, lowp_dtype
     return lib().lens_flow_step(x, v_cond, v_uncond, n, dt, cfg_scale, x_lowp_out, lowp_dtype, stream)
 
 
-def lens_timer_start(kind: int) -> int:
-    return lib().lens_timer_start(kind)
+def lens_timer_start(kind_mask: int) -> int:
+    return lib().lens_timer_start(kind_mask)
 
 
 def lens_timer_stop():
-    ms, n = C.c_double(), C.c_int64()
-    st = lib().lens_timer_stop(C.byref(ms), C.byref(n))
-    return st, ms.value, n.value
+    """-> (status, [ms per kernel family], [launches per kernel family])"""
+    ms, n = (C.c_double * LENS_KERNEL_COUNT)(), (C.c_int64 * LENS_KERNEL_COUNT)()
+    st = lib().lens_timer_stop(ms, n)
+    return st, list(ms), list(n)

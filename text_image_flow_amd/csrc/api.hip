@@ -30,8 +30,9 @@ lens_status fail(lens_status s, const char *fmt, ...) {
 
 // ------------------------------------------------------------ kernel timer
 struct Timer {
-  int kind = -1;
+  uint32_t mask = 0;
   std::vector<hipEvent_t> pool;
+  std::vector<int> kind_of;  // family of each recorded event pair
   size_t used = 0;
 } g_timer;
 
@@ -40,7 +41,7 @@ struct Timed {
   bool on;
   hipStream_t st;
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  Timed(lens_kernel_kind k, hipStream_t s) : on(g_timer.kind == (int)k), st(s) {
+  Timed(lens_kernel_kind k, hipStream_t s) : on((g_timer.mask >> (int)k) & 1u), st(s) {
     if (!on) return;
     while (g_timer.pool.size() < g_timer.used + 2) {
       hipEvent_t e;
@@ -50,6 +51,7 @@ struct Timed {
       }
       g_timer.pool.push_back(e);
     }
+    g_timer.kind_of.push_back((int)k);
     e0 = g_timer.pool[g_timer.used++];
     e1 = g_timer.pool[g_timer.used++];
     (void)hipEventRecord(e0, st);
@@ -475,27 +477,32 @@ lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond,
   return LENS_OK;
 }
 
-lens_status lens_timer_start(lens_kernel_kind kind) {
-  if ((int)kind < 0 || (int)kind > (int)LENS_KERNEL_ADALN)
-    return fail(LENS_ERR_INVALID_ARG, "unknown kernel kind %d", (int)kind);
-  g_timer.kind = (int)kind;
+lens_status lens_timer_start(uint32_t mask) {
+  if (mask >> LENS_KERNEL_COUNT) return fail(LENS_ERR_INVALID_ARG, "kernel mask 0x%x has unknown bits", mask);
+  g_timer.mask = mask;
   g_timer.used = 0;
+  g_timer.kind_of.clear();
   return LENS_OK;
 }
 
-lens_status lens_timer_stop(double *total_ms, int64_t *launches) {
-  double ms = 0.0;
+lens_status lens_timer_stop(double *ms, int64_t *launches) {
+  double acc[LENS_KERNEL_COUNT] = {0};
+  int64_t cnt[LENS_KERNEL_COUNT] = {0};
   const size_t n = g_timer.used / 2;
+  g_timer.mask = 0;
+  g_timer.used = 0;
   for (size_t i = 0; i < n; ++i) {
     HIP_TRY(hipEventSynchronize(g_timer.pool[2 * i + 1]));
     float f = 0.f;
     HIP_TRY(hipEventElapsedTime(&f, g_timer.pool[2 * i], g_timer.pool[2 * i + 1]));
-    ms += f;
+    acc[g_timer.kind_of[i]] += f;
+    cnt[g_timer.kind_of[i]] += 1;
   }
-  g_timer.kind = -1;
-  g_timer.used = 0;
-  if (total_ms) *total_ms = ms;
-  if (launches) *launches = (int64_t)n;
+  g_timer.kind_of.clear();
+  for (int k = 0; k < LENS_KERNEL_COUNT; ++k) {
+    if (ms) ms[k] = acc[k];
+    if (launches) launches[k] = cnt[k];
+  }
   return LENS_OK;
 }
 
