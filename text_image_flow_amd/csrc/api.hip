@@ -243,7 +243,9 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   const int Sp = s_pad(Si, St);
   QkRopeArgs qa{ws.qkv_img, ws.qkv_txt, w->img.q_gain, w->img.k_gain, w->txt.q_gain, w->txt.k_gain, img_pos, txt_pos,
                 ws.Q, ws.K, ws.Vt, B, c->heads, Si, St, Sp, c->rope_axes[0], c->rope_axes[1], c->rope_axes[2],
-                c->rope_theta, c->eps};
+                c->rope_theta, c->eps,
+                bf ? 0.125f * 1.4426950408889634f : 1.0f,   // bf16 attention takes Q in log2 units
+                bf ? 1 : 0};
   {
     Timed t(LENS_KERNEL_QKNORM_ROPE, st);
     e = t.done(launch_qknorm_rope(qa, bf, st));

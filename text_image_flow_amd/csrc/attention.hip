@@ -18,10 +18,10 @@
 //     one exchange with the partner lane (lane ^ 32) and the row sum none
 //     until the end;
 //   * P^T is rounded to bf16 in registers and used directly as the B operand
-//     of O^T += V^T P^T (V is stored transposed, [64, S_pad], so V^T
-//     fragments are plain LDS reads); O^T keeps one query per lane, so the
-//     online-softmax rescale is a per-lane scalar;
-//   * exponentials are exp2 of (s * scale * log2 e - m), one FMA per score.
+//     of O^T += V^T P^T (V stored transposed, [64, S_pad]); O^T keeps one
+//     query per lane, so the online-softmax rescale is a per-lane scalar;
+//   * Q arrives pre-scaled by scale * log2(e), so p = exp2(s - m);
+//   * the grid is flat and XCD-aware (one head's q-blocks share an L2).
 // fp32 path: one thread per query, plain loops (correctness only).
 #include "common.h"
 
@@ -31,7 +31,6 @@ namespace {
 
 constexpr int KV_T = 64;        // keys per tile
 constexpr int LROW = 64 + 8;    // LDS row stride (bf16 elements)
-constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ int kv_count(const AttnArgs &a, int b) {
   int tl = a.S_txt;
@@ -42,6 +41,20 @@ __device__ __forceinline__ int kv_count(const AttnArgs &a, int b) {
   return a.S_img + tl;
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs.  The grid is flat;
+// logical block L = (b, h, q-block) with q-block fastest, and XCD x runs the
+// contiguous logical range [x * n / 8, (x + 1) * n / 8), so the q-blocks of
+// one head share that XCD's L2 copy of the head's K and V.
+__device__ __forceinline__ void attn_block_coords(int nqb, int H, int &qb, int &h, int &b) {
+  const int n = gridDim.x;
+  int bid = blockIdx.x;
+  const int per = n / 8;
+  if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
+  qb = bid % nqb;
+  h = (bid / nqb) % H;
+  b = bid / (nqb * H);
+}
+
 template <typename T>
 __device__ __forceinline__ T *out_row(const AttnArgs &a, int b, int p) {
   const int D = a.H * 64;
@@ -49,35 +62,136 @@ __device__ __forceinline__ T *out_row(const AttnArgs &a, int b, int p) {
   return (T *)a.O_txt + ((int64_t)b * a.S_txt + (p - a.S_img)) * D;
 }
 
-__global__ __launch_bounds__(256) void attn_bf16_mfma(AttnArgs a) {
+// -------------------------------------------------------------- bf16
+// Inputs as the bf16 joint layout above, with two differences the QK-norm
+// kernel provides: Q is pre-multiplied by scale * log2(e), so S = Q K^T is
+// already in log2 units, and within every 16 keys of V^T the key index has
+// bits 2 and 3 swapped, so the 8 keys one lane feeds into a PV k-step are
+// contiguous (one 16-byte LDS read per V^T fragment).
+//
+// A wave owns G groups of 32 queries; every K and V^T fragment read from
+// LDS feeds G MFMAs.  The running max is lazy: rows rescale only when a
+// tile's max exceeds the running max by more than TAU (log2 units), so
+// probabilities stay <= 2^TAU, and most tiles skip the O rescale.  Row sums
+// add the bf16-rounded probabilities with v_dot2 (the same values the PV
+// MFMA consumes).
+constexpr float TAU = 8.0f;
+
+// One KV tile of the v2 kernel for G query groups; MASK handles the last,
+// partial tile (keys >= n_kv get probability 0).
+template <int G, bool MASK>
+__device__ __forceinline__ void attn_tile(const bf16 *sKb, const bf16 *sVb, const bf16x8 (&qf)[G][4],
+                                          f32x16 (&o)[G][2], float (&m_run)[G], float (&l_run)[G], int kv0,
+                                          int n_kv, int ql, int hl) {
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  // S^T (log2 units) for keys kv0 + [0, 32) (s[g][0]) and kv0 + [32, 64) (s[g][1])
+  f32x16 s[G][2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    s[g][0] = f32x16{};
+    s[g][1] = f32x16{};
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 k0 = *(const bf16x8 *)&sKb[ql * LROW + ks * 16 + hl * 8];
+    const bf16x8 k1 = *(const bf16x8 *)&sKb[(32 + ql) * LROW + ks * 16 + hl * 8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      s[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[g][ks], s[g][0], 0, 0, 0);
+      s[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[g][ks], s[g][1], 0, 0, 0);
+    }
+  }
+  if (MASK && kv0 + KV_T > n_kv) {
+    // key of s[g][0][r]: kv0 + (r/4)*8 + hl*4 + r%4; of s[g][1][r]: that + 32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kv = kv0 + (r >> 2) * 8 + hl * 4 + (r & 3);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (kv >= n_kv) s[g][0][r] = -INFINITY;
+        if (kv + 32 >= n_kv) s[g][1][r] = -INFINITY;
+      }
+    }
+  }
+  bf16x8 pb[G][4];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = fmaxf(s[g][0][0], s[g][1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[g][0][r]), s[g][1][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run[g] + TAU)) {
+      const float m_new = fmaxf(m_run[g], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+      m_run[g] = m_new;
+      l_run[g] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o[g][0][r] *= alpha;
+        o[g][1][r] *= alpha;
+      }
+    }
+    const float m = m_run[g];
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      bf16x2 p0 = {(bf16)__builtin_amdgcn_exp2f(s[g][0][e] - m), (bf16)__builtin_amdgcn_exp2f(s[g][0][e + 1] - m)};
+      bf16x2 p1 = {(bf16)__builtin_amdgcn_exp2f(s[g][0][8 + e] - m), (bf16)__builtin_amdgcn_exp2f(s[g][0][9 + e] - m)};
+      bf16x2 p2 = {(bf16)__builtin_amdgcn_exp2f(s[g][1][e] - m), (bf16)__builtin_amdgcn_exp2f(s[g][1][e + 1] - m)};
+      bf16x2 p3 = {(bf16)__builtin_amdgcn_exp2f(s[g][1][8 + e] - m), (bf16)__builtin_amdgcn_exp2f(s[g][1][9 + e] - m)};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(p3, ones, lsum, false);
+      pb[g][0][e] = p0[0]; pb[g][0][e + 1] = p0[1];
+      pb[g][1][e] = p1[0]; pb[g][1][e + 1] = p1[1];
+      pb[g][2][e] = p2[0]; pb[g][2][e + 1] = p2[1];
+      pb[g][3][e] = p3[0]; pb[g][3][e + 1] = p3[1];
+    }
+    l_run[g] += lsum;
+  }
+  // O^T += V^T P^T: the permuted V^T row holds this lane's 8 keys of k-step ks contiguously
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 v0 = *(const bf16x8 *)&sVb[ql * LROW + ks * 16 + hl * 8];
+    const bf16x8 v1 = *(const bf16x8 *)&sVb[(32 + ql) * LROW + ks * 16 + hl * 8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      o[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb[g][ks], o[g][0], 0, 0, 0);
+      o[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb[g][ks], o[g][1], 0, 0, 0);
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void attn_bf16_v2(AttnArgs a) {
+  constexpr int QW = 32 * G, QB = 4 * QW;
   __shared__ __attribute__((aligned(16))) bf16 sK[2][KV_T * LROW];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][64 * LROW];
 
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S_img + a.S_txt;
-  const int q0 = blockIdx.x * 128 + wave * 32;
+  int qb, h, b;
+  attn_block_coords((S + QB - 1) / QB, a.H, qb, h, b);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q0 = qb * QB + wave * QW;
   const int64_t bh = (int64_t)b * a.H + h;
   const bf16 *Qg = (const bf16 *)a.Q + bh * a.S_pad * 64;
   const bf16 *Kg = (const bf16 *)a.K + bh * a.S_pad * 64;
   const bf16 *Vg = (const bf16 *)a.Vt + bh * 64 * a.S_pad;
   const int n_kv = kv_count(a, b);
   const int n_tiles = (n_kv + KV_T - 1) / KV_T;
-  const float c = a.scale * LOG2E;
+  const int hl = lane >> 5, ql = lane & 31;
 
-  const int hl = lane >> 5;      // which half of the wave
-  const int ql = lane & 31;      // this lane's query within the wave
-  // Q^T fragments (B operand): query row, 8 head dims per k-step of 16
-  bf16x8 qf[4];
-  {
-    int qr = q0 + ql;
+  bf16x8 qf[G][4];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    int qr = q0 + g * 32 + ql;
     qr = qr < S ? qr : S - 1;
     const bf16 *src = Qg + (int64_t)qr * 64 + hl * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const bf16x8 *)(src + ks * 16);
+    for (int ks = 0; ks < 4; ++ks) qf[g][ks] = *(const bf16x8 *)(src + ks * 16);
   }
 
-  // tile staging: 2 K chunks + 2 V^T chunks of 16 bytes per thread
   const int lr = tid >> 3, lc = (tid & 7) * 8;
   const bf16 *k_src0 = Kg + (int64_t)lr * 64 + lc;
   const bf16 *k_src1 = Kg + (int64_t)(lr + 32) * 64 + lc;
@@ -91,8 +205,15 @@ __global__ __launch_bounds__(256) void attn_bf16_mfma(AttnArgs a) {
   *(u32x4 *)&sV[0][l_off0] = rv0;
   *(u32x4 *)&sV[0][l_off1] = rv1;
 
-  f32x16 o0 = {}, o1 = {};
-  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[G][2];
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    o[g][0] = f32x16{};
+    o[g][1] = f32x16{};
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+  }
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
@@ -105,71 +226,7 @@ __global__ __launch_bounds__(256) void attn_bf16_mfma(AttnArgs a) {
       rv0 = *(const u32x4 *)(v_src0 + vo);
       rv1 = *(const u32x4 *)(v_src1 + vo);
     }
-    const bf16 *sKb = sK[buf];
-    const bf16 *sVb = sV[buf];
-
-    // S^T for keys kv0 + [0, 32) (s0) and kv0 + [32, 64) (s1)
-    f32x16 s0 = {}, s1 = {};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 k0 = *(const bf16x8 *)&sKb[ql * LROW + ks * 16 + hl * 8];
-      const bf16x8 k1 = *(const bf16x8 *)&sKb[(32 + ql) * LROW + ks * 16 + hl * 8];
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
-    }
-    // key index of s0[r]: kv0 + (r/4)*8 + hl*4 + r%4; of s1[r]: that + 32
-    if (kv0 + KV_T > n_kv) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kv = kv0 + (r >> 2) * 8 + hl * 4 + (r & 3);
-        if (kv >= n_kv) s0[r] = -INFINITY;
-        if (kv + 32 >= n_kv) s1[r] = -INFINITY;
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    // P^T as bf16 B operands: pb[ks] holds keys ks*16 + (e/4)*8 + hl*4 + e%4
-    bf16x8 pb0, pb1, pb2, pb3;
-    float ls = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[e], c, -m_new));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s0[8 + e], c, -m_new));
-      const float p2 = __builtin_amdgcn_exp2f(fmaf(s1[e], c, -m_new));
-      const float p3 = __builtin_amdgcn_exp2f(fmaf(s1[8 + e], c, -m_new));
-      ls += (p0 + p1) + (p2 + p3);
-      pb0[e] = (bf16)p0;
-      pb1[e] = (bf16)p1;
-      pb2[e] = (bf16)p2;
-      pb3[e] = (bf16)p3;
-    }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      o0[r] *= alpha;
-      o1[r] *= alpha;
-    }
-
-    // O^T[d, q] += V^T[d, kv] P^T[kv, q]; k-slot (hl, e) is key
-    // ks*16 + (e/4)*8 + hl*4 + e%4 in both operands.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 pb = ks == 0 ? pb0 : ks == 1 ? pb1 : ks == 2 ? pb2 : pb3;
-      const bf16 *r0 = &sVb[ql * LROW + ks * 16 + hl * 4];
-      const bf16 *r1 = &sVb[(32 + ql) * LROW + ks * 16 + hl * 4];
-      const bf16x4 a0 = *(const bf16x4 *)r0, b0 = *(const bf16x4 *)(r0 + 8);
-      const bf16x4 a1 = *(const bf16x4 *)r1, b1 = *(const bf16x4 *)(r1 + 8);
-      const bf16x8 v0 = {a0[0], a0[1], a0[2], a0[3], b0[0], b0[1], b0[2], b0[3]};
-      const bf16x8 v1 = {a1[0], a1[1], a1[2], a1[3], b1[0], b1[1], b1[2], b1[3]};
-      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb, o0, 0, 0, 0);
-      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb, o1, 0, 0, 0);
-    }
+    attn_tile<G, true>(sK[buf], sV[buf], qf, o, m_run, l_run, kv0, n_kv, ql, hl);
     if (more) {
       *(u32x4 *)&sK[buf ^ 1][l_off0] = rk0;
       *(u32x4 *)&sK[buf ^ 1][l_off1] = rk1;
@@ -179,21 +236,24 @@ __global__ __launch_bounds__(256) void attn_bf16_mfma(AttnArgs a) {
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  const int p = q0 + ql;
-  if (p >= S) return;
-  bf16 *dst = out_row<bf16>(a, b, p) + h * 64;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    bf16x4 v0, v1;
+  for (int g = 0; g < G; ++g) {
+    const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32);
+    const float inv = 1.0f / l_tot;
+    const int p = q0 + g * 32 + ql;
+    if (p >= S) continue;
+    bf16 *dst = out_row<bf16>(a, b, p) + h * 64;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v0[e] = (bf16)(o0[g * 4 + e] * inv);
-      v1[e] = (bf16)(o1[g * 4 + e] * inv);
+    for (int gg = 0; gg < 4; ++gg) {
+      bf16x4 v0, v1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v0[e] = (bf16)(o[g][0][gg * 4 + e] * inv);
+        v1[e] = (bf16)(o[g][1][gg * 4 + e] * inv);
+      }
+      *(bf16x4 *)(dst + gg * 8 + hl * 4) = v0;
+      *(bf16x4 *)(dst + 32 + gg * 8 + hl * 4) = v1;
     }
-    *(bf16x4 *)(dst + g * 8 + hl * 4) = v0;
-    *(bf16x4 *)(dst + 32 + g * 8 + hl * 4) = v1;
   }
 }
 
@@ -246,7 +306,7 @@ __global__ __launch_bounds__(64) void attn_f32_simple(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs &a, bool bf16_path, hipStream_t stream) {
   const int S = a.S_img + a.S_txt;
   if (bf16_path) {
-    hipLaunchKernelGGL(attn_bf16_mfma, dim3((S + 127) / 128, a.H, a.B), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_bf16_v2<1>, dim3(((S + 127) / 128) * a.H * a.B), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL(attn_f32_simple, dim3((S + 63) / 64, a.H, a.B), dim3(64), 0, stream, a);
   }

@@ -167,8 +167,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
       sincosf(ang, &sn, &cs);
       const float q0 = q[i] * rq * to_f32(qg[d]), q1 = q[i + 1] * rq * to_f32(qg[d + 1]);
       const float k0 = k[i] * rk * to_f32(kg[d]), k1 = k[i + 1] * rk * to_f32(kg[d + 1]);
-      q[i] = q0 * cs - q1 * sn;
-      q[i + 1] = q0 * sn + q1 * cs;
+      q[i] = (q0 * cs - q1 * sn) * a.q_scale;
+      q[i + 1] = (q0 * sn + q1 * cs) * a.q_scale;
       k[i] = k0 * cs - k1 * sn;
       k[i + 1] = k0 * sn + k1 * cs;
     }
@@ -177,11 +177,15 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
   store16<T>(Ko, k);
   for (int i = 0; i < 16; ++i) sV[d0 + i][tok] = v[i];
   __syncthreads();
-  // V^T [d][p]: thread t writes d = t/4, positions (t%4)*16 .. +16
+  // V^T [d][p]: thread t writes d = t/4, positions (t%4)*16 .. +16; with
+  // v_perm, position j of the 16 holds key j with bits 2 and 3 swapped
   {
     const int d = t >> 2, c0 = (t & 3) * 16;
     float tmp[16];
-    for (int i = 0; i < 16; ++i) tmp[i] = sV[d][c0 + i];
+    for (int i = 0; i < 16; ++i) {
+      const int src = a.v_perm ? ((i & 3) | ((i & 4) << 1) | ((i & 8) >> 1)) : i;
+      tmp[i] = sV[d][c0 + src];
+    }
     store16<T>((T *)a.Vt + (bh * 64 + d) * a.S_pad + blockIdx.x * 64 + c0, tmp);
   }
 }
