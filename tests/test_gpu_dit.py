@@ -1,0 +1,204 @@
+"""GPU parity of lens_dit_forward, lens_flow_step and the sampler loop
+against the fp64 oracle on the same seeded inputs.
+
+Whole-model parity runs where the oracle finishes in seconds: two blocks at
+small token counts, and one block at the real 1024^2 / 1440^2 / 2:1 and 1:2
+shapes (embeddings, a block and the final layer all at full size).  The full
+48-block model at 1024^2 with the cond/uncond batch of 2 (the benchmarked
+launch) is checked through properties that hold at any size: finite output,
+bit-identical reruns, and exact sample-swap symmetry (batch independence)."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _env():
+    import text_image_flow_amd as T
+    from text_image_flow_amd import device as dv
+    dv.require_gpu()
+    return T, dv
+
+
+def make_inputs(B, gh, gw, St, dtype, txt_len=None, t=None, seed_lat=synth.SEED_LATENT):
+    x = synth.latents(B, gh * gw, seed=seed_lat)
+    x = synth.bf16_round(x) if dtype == "bf16" else x
+    feats = synth.text_features(B, St, dtype=dtype, txt_len=txt_len) if St else np.zeros((B, 0, 11520), np.float32)
+    t = np.linspace(0.9, 0.2, B).astype(np.float32) if t is None else np.asarray(t, np.float32)
+    return x, feats, t, synth.image_positions(gh, gw), synth.text_positions(St)
+
+
+def gpu_dit(n_blocks, dtype, x, feats, t, ip, tp, txt_len, blocks=None, top=None):
+    T, dv = _env()
+    act = T.LENS_BF16 if dtype == "bf16" else T.LENS_F32
+    cfg = T.default_config(act)
+    cfg.n_blocks = n_blocks
+    top = synth.top_weights(dtype=dtype) if top is None else top
+    blocks = [synth.block_weights(i, dtype=dtype) for i in range(n_blocks)] if blocks is None else blocks
+    dit = dv.DeviceDit(top, blocks, act)
+    B, Si = x.shape[:2]
+    St = feats.shape[1]
+    v = torch.empty((B, Si, cfg.out_ch), dtype=torch.float32, device="cuda")
+    d_tl = dv.upload(np.asarray(txt_len, np.int32)) if txt_len is not None else None
+    dv.dit_forward(cfg, dit, dv.upload(x, act), dv.upload(feats, act) if St else None, dv.upload(t), dv.upload(ip),
+                   dv.upload(tp) if St else None, d_tl, v, dv.Workspace())
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), top, blocks
+
+
+def check_dit(n_blocks, dtype, B, gh, gw, St, txt_len=None, t=None):
+    print(f"dit n_blocks={n_blocks} {dtype} B={B} grid={gh}x{gw} S_txt={St} txt_len={txt_len}", flush=True)
+    x, feats, t, ip, tp = make_inputs(B, gh, gw, St, dtype, txt_len, t)
+    v, top, blocks = gpu_dit(n_blocks, dtype, x, feats, t, ip, tp, txt_len)
+    ref = O.dit_forward(top, blocks, x, feats, t, ip, tp, txt_len)
+    assert_parity(v, ref, f"v ({n_blocks} blocks, {dtype})")
+
+
+def test_dit_two_blocks_bf16_masked():
+    check_dit(2, "bf16", 2, 8, 10, 24, txt_len=[24, 9])
+
+
+def test_dit_two_blocks_f32():
+    check_dit(2, "f32", 1, 7, 9, 16)
+
+
+def test_dit_no_blocks_1024():
+    """Embeddings and final layer alone at 1024^2, B = 2."""
+    check_dit(0, "bf16", 2, 64, 64, 512)
+
+
+def test_dit_one_block_1024_cfg_batch():
+    """img_in / txt_in / one block / final layer at 1024^2 with the cond and
+    uncond text of the CFG batch (independent seeded feature draws)."""
+    T, dv = _env()
+    x, _, t, ip, tp = make_inputs(2, 64, 64, 512, "bf16", t=[0.55, 0.55])
+    x[1] = x[0]
+    feats = np.concatenate([synth.text_features(1, 512, seed=synth.SEED_TEXT_COND),
+                            synth.text_features(1, 512, seed=synth.SEED_TEXT_UNCOND)])
+    v, top, blocks = gpu_dit(1, "bf16", x, feats, t, ip, tp, None)
+    ref = O.dit_forward(top, blocks, x, feats, t, ip, tp, None)
+    assert_parity(v, ref, "v (1 block, 1024^2, cond+uncond)")
+
+
+def test_dit_one_block_1440():
+    """1440^2: 90 x 90 = 8100 image tokens + 512 text tokens, B = 1."""
+    check_dit(1, "bf16", 1, 90, 90, 512, t=[1.0])
+
+
+@pytest.mark.parametrize("gh,gw", [(45, 90), (90, 45)])
+def test_dit_one_block_aspect_masked_batch8(gh, gw):
+    """2:1 and 1:2 aspect (4050 image tokens), batch 8 (4 cond + 4 uncond),
+    text lengths drawn from 64..512 and padded to 512 with the key mask."""
+    tl = np.concatenate([synth.text_lengths(4, 64, 512, stream=0), synth.text_lengths(4, 64, 512, stream=1)])
+    check_dit(1, "bf16", 8, gh, gw, 512, txt_len=tl, t=[0.8] * 8)
+
+
+def test_dit_full_48_blocks_1024_properties():
+    """The benchmarked launch: 48 blocks, 1024^2, cond + uncond batch of 2.
+    Output is finite, a rerun is bit-identical, and swapping the two
+    samples' inputs swaps the outputs exactly (no cross-sample leakage)."""
+    T, dv = _env()
+    cfg = T.default_config(T.LENS_BF16)
+    dit = dv.DeviceDit(synth.top_weights(), [w for _, w in synth.all_block_weights(threads=16)], T.LENS_BF16)
+    x0 = synth.bf16_round(synth.latents(1, 4096))
+    xa = np.concatenate([x0, synth.bf16_round(synth.latents(1, 4096, sample=1))])
+    fa = np.concatenate([synth.text_features(1, 512, seed=synth.SEED_TEXT_COND),
+                         synth.text_features(1, 512, seed=synth.SEED_TEXT_UNCOND)])
+    ip, tp = dv.upload(synth.image_positions(64, 64)), dv.upload(synth.text_positions(512))
+    ws = dv.Workspace()
+
+    def run(x, f, t):
+        v = torch.empty((2, 4096, 128), dtype=torch.float32, device="cuda")
+        dv.dit_forward(cfg, dit, dv.upload(x, T.LENS_BF16), dv.upload(f, T.LENS_BF16), dv.upload(t), ip, tp, None,
+                       v, ws)
+        torch.cuda.synchronize()
+        return v.cpu().numpy()
+
+    t = np.array([0.75, 0.35], np.float32)
+    v1 = run(xa, fa, t)
+    assert np.all(np.isfinite(v1)) and np.std(v1) > 0
+    v2 = run(xa, fa, t)
+    assert np.array_equal(v1, v2), "rerun is not bit-identical"
+    vs = run(xa[::-1].copy(), fa[::-1].copy(), t[::-1].copy())
+    assert np.array_equal(vs[0], v1[1]) and np.array_equal(vs[1], v1[0]), "sample swap changed the outputs"
+
+
+# ------------------------------------------------------------ flow step
+@pytest.mark.parametrize("cfg_scale,use_uncond", [(5.0, True), (1.0, False), (1.0, True)])
+def test_flow_step_1024(cfg_scale, use_uncond):
+    T, dv = _env()
+    n = 4096 * 128
+    x = synth.gaussian((n,), 2, 0)
+    vc, vu = synth.gaussian((n,), 2, 1), synth.gaussian((n,), 2, 2)
+    dx = dv.upload(x)
+    lowp = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    dv.flow_step(dx, dv.upload(vc), dv.upload(vu) if use_uncond else None, -0.05, cfg_scale, lowp)
+    torch.cuda.synchronize()
+    ref = O.flow_step(x, vc, vu if use_uncond else None, -0.05, cfg_scale)
+    g = dx.cpu().numpy()
+    assert_parity(g, ref, f"flow step s={cfg_scale} uncond={use_uncond}")
+    assert np.max(np.abs(g - ref)) <= 4e-6 * np.max(np.abs(ref))
+    # the bf16 copy is the round-to-nearest-even of the new x
+    assert np.array_equal(lowp.float().cpu().numpy(), synth.bf16_round(g))
+
+
+# ------------------------------------------------------------ sampler
+def _small_sampler_setup(use_cfg):
+    T, dv = _env()
+    gh, gw, St = 8, 8, 16
+    cfg = T.default_config(T.LENS_BF16)
+    cfg.n_blocks = 2
+    top = synth.top_weights()
+    blocks = [synth.block_weights(i) for i in range(2)]
+    dit = dv.DeviceDit(top, blocks, T.LENS_BF16)
+    n = 1
+    fc = synth.text_features(1, St, seed=synth.SEED_TEXT_COND)
+    fu = synth.text_features(1, St, seed=synth.SEED_TEXT_UNCOND)
+    feats = np.concatenate([fc, fu]) if use_cfg else fc
+    ip, tp = synth.image_positions(gh, gw), synth.text_positions(St)
+    x0 = synth.latents(n, gh * gw)
+    smp = dv.Sampler(cfg, dit, dv.upload(ip), dv.upload(tp), n, gh * gw, St, 5.0 if use_cfg else 1.0, use_cfg)
+    return dv, top, blocks, feats, ip, tp, x0, smp
+
+
+def test_sampler_cfg_teacher_forced():
+    """Each CFG Euler step from the GPU's own state: x_{k+1} - x_k against
+    dt * (v_u + 5 (v_c - v_u)) from the oracle at the same bf16 input."""
+    dv, top, blocks, feats, ip, tp, x0, smp = _small_sampler_setup(True)
+    steps = 3
+    states = []
+    x = dv.upload(x0)
+    smp.run(x, dv.upload(synth.bf16_round(x0), 1), dv.upload(feats, 1), None, steps,
+            step_hook=lambda k, xs, xa: states.append((xs.cpu().numpy().copy(), xa.float().cpu().numpy().copy())))
+    torch.cuda.synchronize()
+    states.append((x.cpu().numpy(), None))
+    ts = O.time_grid(steps)
+    for k in range(steps):
+        xk, xa = states[k]
+        assert np.array_equal(xa[0], synth.bf16_round(xk[0])) and np.array_equal(xa[1], xa[0])
+        t = np.array([ts[k], ts[k]])
+        v = O.dit_forward(top, blocks, xa, feats, t, ip, tp)
+        ref = O.flow_step(xk[0], v[0], v[1], ts[k + 1] - ts[k], 5.0)
+        assert_parity(states[k + 1][0][0], ref, f"x_{k + 1}")
+        # the increment carries the whole step; CFG 5 amplifies velocity
+        # rounding by up to 5 + 4, so it gets the block-delta bar
+        assert_parity(states[k + 1][0][0] - xk[0], ref - xk[0], f"dx_{k}", rel=5e-2)
+
+
+def test_sampler_turbo_free_running():
+    """Four Euler steps without CFG from the same N(0,1) latent: final x."""
+    dv, top, blocks, feats, ip, tp, x0, smp = _small_sampler_setup(False)
+    x = dv.upload(x0)
+    smp.run(x, dv.upload(synth.bf16_round(x0), 1), dv.upload(feats, 1), None, 4)
+    torch.cuda.synchronize()
+
+    def vel(xs, t):
+        return O.dit_forward(top, blocks, synth.bf16_round(xs.astype(np.float32)), feats, np.array([t]), ip, tp)
+
+    ref = O.sample(vel, x0, 4)
+    assert_parity(x.cpu().numpy(), ref, "x after 4 steps")
