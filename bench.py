@@ -62,6 +62,28 @@ def step_flops(d, S_img, S_txt, B):
             "total": d.n_blocks * (g + a + m) + emb + tmlp}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dit_step_1024_traffic.md")
+GEMM_SRC = os.path.join(ROOT, "text_image_flow_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when that summary is missing or was taken on
+    a different GEMM source than the one built now."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines() if l.startswith(("traffic_bytes_per_launch:", "gemm_source_sha256:")))
+    if not fields:
+        return None
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    if fields.get("gemm_source_sha256", "").strip() != sha:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(d):
     """The oracle as it stands, on one block at 1024^2 (B = 1), fp64."""
     import oracle as O
@@ -91,6 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timer", action="store_true")
+    ap.add_argument("--copy-kernel-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the path has no multi-GPU part (asked for --gpus {args.gpus})",
@@ -98,6 +122,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_kernel_bytes:
+        n = args.copy_kernel_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_kernel_bytes": n * 4, "launches": 3}))
+        return
 
     import synth
     import text_image_flow_amd as T
@@ -183,8 +217,9 @@ def main():
         per_launch_flops = fam_flops[dom] / (n[i] / args.steps)
         avg_s = ms[i] / n[i] * 1e-3
         ach = per_launch_flops / avg_s / 1e12
+        traffic = measured_traffic() if dom == "gemm" else None
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flops_per_launch": per_launch_flops, "avg_launch_us": round(avg_s * 1e6, 2)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(d)
