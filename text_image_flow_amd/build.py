@@ -44,6 +44,11 @@ def _run(cmd):
     return err
 
 
+# per-source extra flags: the attention kernel keeps its MFMA accumulators in
+# VGPRs (the softmax reads them with VALU instructions every tile)
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
@@ -52,7 +57,7 @@ def build(verbose: bool = False) -> str:
     for s in SOURCES:
         o = os.path.join(BUILD, s.replace(".hip", ".o"))
         objs.append(o)
-        jobs.append([cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        jobs.append([cc, *FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o])
     with ThreadPoolExecutor(len(jobs)) as ex:
         for msg in ex.map(_run, jobs):
             if verbose and msg.strip():

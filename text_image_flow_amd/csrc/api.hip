@@ -103,8 +103,8 @@ lens_status check_dit_config(const lens_config *c) {
     return fail(LENS_ERR_UNSUPPORTED, "out_ch %d: must be a positive multiple of 128", c->out_ch);
   if (c->txt_layers <= 0 || c->txt_feat_dim <= 0 || (c->txt_layers * c->txt_feat_dim) % 64)
     return fail(LENS_ERR_UNSUPPORTED, "txt_layers * txt_feat_dim must be a positive multiple of 64");
-  if (c->t_freq_dim <= 0 || c->t_freq_dim % 16)
-    return fail(LENS_ERR_UNSUPPORTED, "t_freq_dim %d: must be a positive multiple of 16", c->t_freq_dim);
+  if (c->t_freq_dim <= 0 || c->t_freq_dim % 16 || c->t_freq_dim > 2048)
+    return fail(LENS_ERR_UNSUPPORTED, "t_freq_dim %d: must be a positive multiple of 16, at most 2048", c->t_freq_dim);
   return LENS_OK;
 }
 

@@ -12,7 +12,7 @@
 //
 // bf16 path (flash-style, one pass over K/V):
 //   * a wave owns 32 queries; four waves share 64-key K and V^T tiles that
-//     are double-buffered in LDS;
+//     direct global->LDS loads double-buffer in LDS;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane then holds one
 //     query (lane & 31) and 32 of the tile's 64 keys, so the row max needs
 //     one exchange with the partner lane (lane ^ 32) and the row sum none
@@ -20,7 +20,9 @@
 //   * P^T is rounded to bf16 in registers and used directly as the B operand
 //     of O^T += V^T P^T (V stored transposed, [64, S_pad]); O^T keeps one
 //     query per lane, so the online-softmax rescale is a per-lane scalar;
-//   * Q arrives pre-scaled by scale * log2(e), so p = exp2(s - m);
+//   * Q arrives pre-scaled by scale * log2(e), and the QK MFMAs start from
+//     -m, so p = exp2(s) with no subtraction; the running max is lazy and
+//     row sums add the bf16 probabilities with v_dot2;
 //   * the grid is flat and XCD-aware (one head's q-blocks share an L2).
 // fp32 path: one thread per query, plain loops (correctness only).
 #include "common.h"
@@ -30,7 +32,6 @@ namespace lens {
 namespace {
 
 constexpr int KV_T = 64;        // keys per tile
-constexpr int LROW = 64 + 8;    // LDS row stride (bf16 elements)
 
 __device__ __forceinline__ int kv_count(const AttnArgs &a, int b) {
   int tl = a.S_txt;
@@ -62,198 +63,206 @@ __device__ __forceinline__ T *out_row(const AttnArgs &a, int b, int p) {
   return (T *)a.O_txt + ((int64_t)b * a.S_txt + (p - a.S_img)) * D;
 }
 
-// -------------------------------------------------------------- bf16
-// Inputs as the bf16 joint layout above, with two differences the QK-norm
-// kernel provides: Q is pre-multiplied by scale * log2(e), so S = Q K^T is
-// already in log2 units, and within every 16 keys of V^T the key index has
-// bits 2 and 3 swapped, so the 8 keys one lane feeds into a PV k-step are
-// contiguous (one 16-byte LDS read per V^T fragment).
-//
-// A wave owns G groups of 32 queries; every K and V^T fragment read from
-// LDS feeds G MFMAs.  The running max is lazy: rows rescale only when a
-// tile's max exceeds the running max by more than TAU (log2 units), so
-// probabilities stay <= 2^TAU, and most tiles skip the O rescale.  Row sums
-// add the bf16-rounded probabilities with v_dot2 (the same values the PV
-// MFMA consumes).
+// Lazy running max: rows rescale only when a tile's max exceeds the running
+// max by more than TAU (log2 units), so probabilities stay <= 2^TAU.
 constexpr float TAU = 8.0f;
 
-// One KV tile of the v2 kernel for G query groups; MASK handles the last,
-// partial tile (keys >= n_kv get probability 0).
-template <int G, bool MASK>
-__device__ __forceinline__ void attn_tile(const bf16 *sKb, const bf16 *sVb, const bf16x8 (&qf)[G][4],
-                                          f32x16 (&o)[G][2], float (&m_run)[G], float (&l_run)[G], int kv0,
-                                          int n_kv, int ql, int hl) {
+// -------------------------------------------------------------- bf16
+// K and V^T tiles arrive by direct
+// global->LDS loads (global_load_lds_dwordx4: one wave instruction fills 1 KB
+// = 8 rows of 128 bytes) into a double-buffered ring, so no VGPRs stage
+// them.  Rows are unpadded; 16-byte chunk c of row r sits in slot
+// c ^ (r & 7), which spreads the 32 rows of a fragment read over the banks.
+// The partial last tile is peeled so the steady-state loop carries no mask.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); }
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+// One 64-key tile.  FIRST: the S accumulators start at 0, the tile's max
+// becomes the running max m and p = exp2(s - m).  Otherwise they start at
+// minit = -m (16 copies), so the MFMAs deliver s - m directly and p = exp2(.)
+// needs no subtraction; only when a tile's max exceeds m by more than TAU
+// is m raised (O and l rescaled, this tile's values shifted).
+template <bool FIRST, bool MASK>
+__device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, const bf16x8 (&qf)[4], f32x16 (&o)[2],
+                                             float &m_run, float &l_run, f32x16 &minit, int kv0, int n_kv, int ql,
+                                             int hl) {
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  // S^T (log2 units) for keys kv0 + [0, 32) (s[g][0]) and kv0 + [32, 64) (s[g][1])
-  f32x16 s[G][2];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    s[g][0] = f32x16{};
-    s[g][1] = f32x16{};
+  const int sw = ql & 7;   // rows ql and 32 + ql share the swizzle
+  f32x16 s0, s1;
+  {
+    const int slot = (hl ^ sw) << 4;
+    const bf16x8 k0 = *(const bf16x8 *)(sKb + ql * 128 + slot);
+    const bf16x8 k1 = *(const bf16x8 *)(sKb + (32 + ql) * 128 + slot);
+    const f32x16 c0 = FIRST ? f32x16{} : minit;
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], c0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[0], c0, 0, 0, 0);
   }
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 k0 = *(const bf16x8 *)&sKb[ql * LROW + ks * 16 + hl * 8];
-    const bf16x8 k1 = *(const bf16x8 *)&sKb[(32 + ql) * LROW + ks * 16 + hl * 8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      s[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[g][ks], s[g][0], 0, 0, 0);
-      s[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[g][ks], s[g][1], 0, 0, 0);
-    }
+  for (int ks = 1; ks < 4; ++ks) {
+    const int slot = ((ks * 2 + hl) ^ sw) << 4;
+    const bf16x8 k0 = *(const bf16x8 *)(sKb + ql * 128 + slot);
+    const bf16x8 k1 = *(const bf16x8 *)(sKb + (32 + ql) * 128 + slot);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
   }
-  if (MASK && kv0 + KV_T > n_kv) {
-    // key of s[g][0][r]: kv0 + (r/4)*8 + hl*4 + r%4; of s[g][1][r]: that + 32
+  if constexpr (MASK) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kv = kv0 + (r >> 2) * 8 + hl * 4 + (r & 3);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (kv >= n_kv) s[g][0][r] = -INFINITY;
-        if (kv + 32 >= n_kv) s[g][1][r] = -INFINITY;
-      }
+      if (kv >= n_kv) s0[r] = -INFINITY;
+      if (kv + 32 >= n_kv) s1[r] = -INFINITY;
     }
   }
-  bf16x8 pb[G][4];
+  float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float mx = fmaxf(s[g][0][0], s[g][1][0]);
+  for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if constexpr (FIRST) {
+    m_run = mx;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[g][0][r]), s[g][1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (__any(mx > m_run[g] + TAU)) {
-      const float m_new = fmaxf(m_run[g], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-      m_run[g] = m_new;
-      l_run[g] *= alpha;
+    for (int r = 0; r < 16; ++r) {
+      s0[r] -= mx;
+      s1[r] -= mx;
+      minit[r] = -mx;
+    }
+  } else {
+    if (__any(mx > TAU)) {
+      // raise the running max by this tile's excess (per lane, >= 0)
+      const float d = fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      m_run += d;
+      l_run *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        o[g][0][r] *= alpha;
-        o[g][1][r] *= alpha;
+        o[0][r] *= alpha;
+        o[1][r] *= alpha;
+        s0[r] -= d;
+        s1[r] -= d;
+        minit[r] = -m_run;
       }
     }
-    const float m = m_run[g];
-    float lsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      bf16x2 p0 = {(bf16)__builtin_amdgcn_exp2f(s[g][0][e] - m), (bf16)__builtin_amdgcn_exp2f(s[g][0][e + 1] - m)};
-      bf16x2 p1 = {(bf16)__builtin_amdgcn_exp2f(s[g][0][8 + e] - m), (bf16)__builtin_amdgcn_exp2f(s[g][0][9 + e] - m)};
-      bf16x2 p2 = {(bf16)__builtin_amdgcn_exp2f(s[g][1][e] - m), (bf16)__builtin_amdgcn_exp2f(s[g][1][e + 1] - m)};
-      bf16x2 p3 = {(bf16)__builtin_amdgcn_exp2f(s[g][1][8 + e] - m), (bf16)__builtin_amdgcn_exp2f(s[g][1][9 + e] - m)};
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(p3, ones, lsum, false);
-      pb[g][0][e] = p0[0]; pb[g][0][e + 1] = p0[1];
-      pb[g][1][e] = p1[0]; pb[g][1][e + 1] = p1[1];
-      pb[g][2][e] = p2[0]; pb[g][2][e + 1] = p2[1];
-      pb[g][3][e] = p3[0]; pb[g][3][e + 1] = p3[1];
-    }
-    l_run[g] += lsum;
   }
-  // O^T += V^T P^T: the permuted V^T row holds this lane's 8 keys of k-step ks contiguously
+  bf16x8 pb[4];
+  float lsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    bf16x2 p0 = {(bf16)__builtin_amdgcn_exp2f(s0[e]), (bf16)__builtin_amdgcn_exp2f(s0[e + 1])};
+    bf16x2 p1 = {(bf16)__builtin_amdgcn_exp2f(s0[8 + e]), (bf16)__builtin_amdgcn_exp2f(s0[9 + e])};
+    bf16x2 p2 = {(bf16)__builtin_amdgcn_exp2f(s1[e]), (bf16)__builtin_amdgcn_exp2f(s1[e + 1])};
+    bf16x2 p3 = {(bf16)__builtin_amdgcn_exp2f(s1[8 + e]), (bf16)__builtin_amdgcn_exp2f(s1[9 + e])};
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, lsum, false);
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(p3, ones, lsum, false);
+    pb[0][e] = p0[0]; pb[0][e + 1] = p0[1];
+    pb[1][e] = p1[0]; pb[1][e + 1] = p1[1];
+    pb[2][e] = p2[0]; pb[2][e + 1] = p2[1];
+    pb[3][e] = p3[0]; pb[3][e + 1] = p3[1];
+  }
+  l_run += lsum;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 v0 = *(const bf16x8 *)&sVb[ql * LROW + ks * 16 + hl * 8];
-    const bf16x8 v1 = *(const bf16x8 *)&sVb[(32 + ql) * LROW + ks * 16 + hl * 8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      o[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb[g][ks], o[g][0], 0, 0, 0);
-      o[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb[g][ks], o[g][1], 0, 0, 0);
-    }
+    const int slot = ((ks * 2 + hl) ^ sw) << 4;
+    const bf16x8 v0 = *(const bf16x8 *)(sVb + ql * 128 + slot);
+    const bf16x8 v1 = *(const bf16x8 *)(sVb + (32 + ql) * 128 + slot);
+    o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb[ks], o[0], 0, 0, 0);
+    o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb[ks], o[1], 0, 0, 0);
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void attn_bf16_v2(AttnArgs a) {
-  constexpr int QW = 32 * G, QB = 4 * QW;
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][KV_T * LROW];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][64 * LROW];
+__global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
+  constexpr int TILE_BYTES = 64 * 128;        // K tile or V^T tile
+  constexpr int STAGE = 2 * TILE_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int S = a.S_img + a.S_txt;
   int qb, h, b;
-  attn_block_coords((S + QB - 1) / QB, a.H, qb, h, b);
+  attn_block_coords((S + 127) / 128, a.H, qb, h, b);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q0 = qb * QB + wave * QW;
+  const int q0 = qb * 128 + wave * 32;
   const int64_t bh = (int64_t)b * a.H + h;
   const bf16 *Qg = (const bf16 *)a.Q + bh * a.S_pad * 64;
   const bf16 *Kg = (const bf16 *)a.K + bh * a.S_pad * 64;
   const bf16 *Vg = (const bf16 *)a.Vt + bh * 64 * a.S_pad;
   const int n_kv = kv_count(a, b);
   const int n_tiles = (n_kv + KV_T - 1) / KV_T;
+  const int n_full = n_kv / KV_T;
   const int hl = lane >> 5, ql = lane & 31;
 
-  bf16x8 qf[G][4];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    int qr = q0 + g * 32 + ql;
+  bf16x8 qf[4];
+  {
+    int qr = q0 + ql;
     qr = qr < S ? qr : S - 1;
     const bf16 *src = Qg + (int64_t)qr * 64 + hl * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[g][ks] = *(const bf16x8 *)(src + ks * 16);
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const bf16x8 *)(src + ks * 16);
   }
+  // each wave fills rows [wave * 16, wave * 16 + 16) of the K and V^T tiles:
+  // two instructions of 8 rows each; lane -> row + lane / 8, slot lane % 8
+  const int r0 = wave * 16 + (lane >> 3), r1 = r0 + 8, slot = lane & 7;
+  const bf16 *k_src0 = Kg + (int64_t)r0 * 64 + ((slot ^ (r0 & 7)) * 8);
+  const bf16 *k_src1 = Kg + (int64_t)r1 * 64 + ((slot ^ (r1 & 7)) * 8);
+  const bf16 *v_src0 = Vg + (int64_t)r0 * a.S_pad + ((slot ^ (r0 & 7)) * 8);
+  const bf16 *v_src1 = Vg + (int64_t)r1 * a.S_pad + ((slot ^ (r1 & 7)) * 8);
+  const int dst0 = wave * 16 * 128, dst1 = dst0 + 8 * 128;
+#define ATT_ISSUE(t_)                                                                                       \
+  do {                                                                                                      \
+    char *sb_ = smem + ((t_) & 1) * STAGE;                                                                  \
+    const int64_t ko_ = (int64_t)(t_) * KV_T * 64, vo_ = (int64_t)(t_) * KV_T;                            \
+    __builtin_amdgcn_global_load_lds((const void *)(k_src0 + ko_), (lds_void_t *)(sb_ + dst0), 16, 0, 0);  \
+    __builtin_amdgcn_global_load_lds((const void *)(k_src1 + ko_), (lds_void_t *)(sb_ + dst1), 16, 0, 0);  \
+    __builtin_amdgcn_global_load_lds((const void *)(v_src0 + vo_), (lds_void_t *)(sb_ + TILE_BYTES + dst0), \
+                                     16, 0, 0);                                                             \
+    __builtin_amdgcn_global_load_lds((const void *)(v_src1 + vo_), (lds_void_t *)(sb_ + TILE_BYTES + dst1), \
+                                     16, 0, 0);                                                             \
+  } while (0)
 
-  const int lr = tid >> 3, lc = (tid & 7) * 8;
-  const bf16 *k_src0 = Kg + (int64_t)lr * 64 + lc;
-  const bf16 *k_src1 = Kg + (int64_t)(lr + 32) * 64 + lc;
-  const bf16 *v_src0 = Vg + (int64_t)lr * a.S_pad + lc;
-  const bf16 *v_src1 = Vg + (int64_t)(lr + 32) * a.S_pad + lc;
-  const int l_off0 = lr * LROW + lc, l_off1 = (lr + 32) * LROW + lc;
-  u32x4 rk0 = *(const u32x4 *)k_src0, rk1 = *(const u32x4 *)k_src1;
-  u32x4 rv0 = *(const u32x4 *)v_src0, rv1 = *(const u32x4 *)v_src1;
-  *(u32x4 *)&sK[0][l_off0] = rk0;
-  *(u32x4 *)&sK[0][l_off1] = rk1;
-  *(u32x4 *)&sV[0][l_off0] = rv0;
-  *(u32x4 *)&sV[0][l_off1] = rv1;
-
-  f32x16 o[G][2];
-  float m_run[G], l_run[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    o[g][0] = f32x16{};
-    o[g][1] = f32x16{};
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
+  f32x16 o[2] = {f32x16{}, f32x16{}};
+  f32x16 minit;
+  float m_run = 0.f, l_run = 0.f;
+  ATT_ISSUE(0);
+  // tile 0 (always holds image keys, so at least one valid key per row)
+  wait_vmcnt0();
+  __builtin_amdgcn_s_barrier();
+  if (1 < n_tiles) ATT_ISSUE(1);
+  if (n_full >= 1)
+    attn_tile<true, false>(smem, smem + TILE_BYTES, qf, o, m_run, l_run, minit, 0, n_kv, ql, hl);
+  else
+    attn_tile<true, true>(smem, smem + TILE_BYTES, qf, o, m_run, l_run, minit, 0, n_kv, ql, hl);
+  for (int t = 1; t < n_full; ++t) {
+    wait_vmcnt0();      // this wave's part of tile t has landed
+    wait_lgkmcnt0();    // and its reads of tile t - 1 have returned
+    __builtin_amdgcn_s_barrier();
+    if (t + 1 < n_tiles) ATT_ISSUE(t + 1);
+    const char *sb = smem + (t & 1) * STAGE;
+    attn_tile<false, false>(sb, sb + TILE_BYTES, qf, o, m_run, l_run, minit, t * KV_T, n_kv, ql, hl);
   }
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const int kv0 = t * KV_T;
-    const bool more = t + 1 < n_tiles;
-    if (more) {
-      const int64_t ko = (int64_t)(kv0 + KV_T) * 64, vo = kv0 + KV_T;
-      rk0 = *(const u32x4 *)(k_src0 + ko);
-      rk1 = *(const u32x4 *)(k_src1 + ko);
-      rv0 = *(const u32x4 *)(v_src0 + vo);
-      rv1 = *(const u32x4 *)(v_src1 + vo);
-    }
-    attn_tile<G, true>(sK[buf], sV[buf], qf, o, m_run, l_run, kv0, n_kv, ql, hl);
-    if (more) {
-      *(u32x4 *)&sK[buf ^ 1][l_off0] = rk0;
-      *(u32x4 *)&sK[buf ^ 1][l_off1] = rk1;
-      *(u32x4 *)&sV[buf ^ 1][l_off0] = rv0;
-      *(u32x4 *)&sV[buf ^ 1][l_off1] = rv1;
-    }
-    __syncthreads();
+  if (n_full < n_tiles && n_full >= 1) {
+    wait_vmcnt0();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    const char *sb = smem + (n_full & 1) * STAGE;
+    attn_tile<false, true>(sb, sb + TILE_BYTES, qf, o, m_run, l_run, minit, n_full * KV_T, n_kv, ql, hl);
   }
+#undef ATT_ISSUE
 
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  const int p = q0 + ql;
+  if (p >= S) return;
+  bf16 *dst = out_row<bf16>(a, b, p) + h * 64;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32);
-    const float inv = 1.0f / l_tot;
-    const int p = q0 + g * 32 + ql;
-    if (p >= S) continue;
-    bf16 *dst = out_row<bf16>(a, b, p) + h * 64;
+  for (int gg = 0; gg < 4; ++gg) {
+    bf16x4 v0, v1;
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      bf16x4 v0, v1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v0[e] = (bf16)(o[g][0][gg * 4 + e] * inv);
-        v1[e] = (bf16)(o[g][1][gg * 4 + e] * inv);
-      }
-      *(bf16x4 *)(dst + gg * 8 + hl * 4) = v0;
-      *(bf16x4 *)(dst + 32 + gg * 8 + hl * 4) = v1;
+    for (int e = 0; e < 4; ++e) {
+      v0[e] = (bf16)(o[0][gg * 4 + e] * inv);
+      v1[e] = (bf16)(o[1][gg * 4 + e] * inv);
     }
+    *(bf16x4 *)(dst + gg * 8 + hl * 4) = v0;
+    *(bf16x4 *)(dst + 32 + gg * 8 + hl * 4) = v1;
   }
 }
 
@@ -306,7 +315,7 @@ __global__ __launch_bounds__(64) void attn_f32_simple(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs &a, bool bf16_path, hipStream_t stream) {
   const int S = a.S_img + a.S_txt;
   if (bf16_path) {
-    hipLaunchKernelGGL(attn_bf16_v2<1>, dim3(((S + 127) / 128) * a.H * a.B), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_bf16, dim3(((S + 127) / 128) * a.H * a.B), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL(attn_f32_simple, dim3((S + 63) / 64, a.H, a.B), dim3(64), 0, stream, a);
   }

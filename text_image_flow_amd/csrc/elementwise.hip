@@ -192,56 +192,81 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
 
 // ------------------------------------------------ skinny GEMM (GEMV)
 // y[b, n] = sum_k f(x[b, k]) W[n, k] + bias[n] for b < B (B <= 8 per launch).
-// One wave per output row n, 8 rows per wave; f(x) staged in LDS once.
-constexpr int GEMV_ROWS_PER_WAVE = 8;
+// HBM-bound on W, which is read exactly once for all B samples.  Each wave
+// keeps f(x) for its k-range in registers (lane l owns k = 8 l + 512 i) and
+// handles 8 rows at a time with all of their 16-byte weight loads issued
+// before any FMA, so many loads are in flight per lane.
+constexpr int GEMV_ROWS = 8;      // rows per wave pass
+constexpr int GEMV_WAVES = 4;
 constexpr int GEMV_MAXB = 8;
+constexpr int GEMV_MAXK = 2048;   // K <= 512 * GEMV_KC
+constexpr int GEMV_KC = GEMV_MAXK / 512;
 
 template <typename T, int NB>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvBatch g, const float *x, int K, int silu_in) {
-  extern __shared__ float sx[];  // [NB][K]
   const int prob = blockIdx.y;
   const int N = g.N[prob];
-  const int nbase = blockIdx.x * 4 * GEMV_ROWS_PER_WAVE;
-  if (nbase >= N) return;
-  for (int e = threadIdx.x; e < NB * K; e += 256) {
-    const float v = x[e];
-    sx[e] = silu_in ? silu_f(v) : v;
-  }
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * GEMV_WAVES + wave) * GEMV_ROWS;
+  if (row0 >= N) return;
+  const int nkc = (K + 511) / 512;   // k-chunks of 8 per lane
+  float fx[NB][GEMV_KC][8];
+#pragma unroll
+  for (int c = 0; c < GEMV_KC; ++c) {
+    const int k = c * 512 + lane * 8;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = 0.f;
+        if (c < nkc && k + e < K) {
+          v = x[(int64_t)b * K + k + e];
+          v = silu_in ? silu_f(v) : v;
+        }
+        fx[b][c][e] = v;
+      }
+  }
   const T *W = (const T *)g.W[prob];
   const T *bias = (const T *)g.bias[prob];
-  for (int rr = 0; rr < GEMV_ROWS_PER_WAVE; ++rr) {
-    const int n = nbase + wave * GEMV_ROWS_PER_WAVE + rr;
-    if (n >= N) break;
-    const T *wr = W + (int64_t)n * K;
-    float acc[NB];
+  float acc[GEMV_ROWS][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-    for (int k = lane * 8; k < K; k += 512) {
-      float w[8];
+  for (int r = 0; r < GEMV_ROWS; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+#pragma unroll
+  for (int c = 0; c < GEMV_KC; ++c) {
+    if (c >= nkc) break;
+    const int k = c * 512 + lane * 8;
+    if (k >= K) break;
+    float w[GEMV_ROWS][8];
+#pragma unroll
+    for (int r = 0; r < GEMV_ROWS; ++r) {
+      const int n = row0 + r < N ? row0 + r : N - 1;
+      const T *wr = W + (int64_t)n * K + k;
       if constexpr (sizeof(T) == 2) {
-        const bf16x8 wv = *(const bf16x8 *)(wr + k);
+        const bf16x8 wv = *(const bf16x8 *)wr;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = (float)wv[i];
+        for (int e = 0; e < 8; ++e) w[r][e] = (float)wv[e];
       } else {
-        const float4 a = *(const float4 *)(wr + k), c = *(const float4 *)(wr + k + 4);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float *xb = sx + b * K + k;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[b] = fmaf(w[i], xb[i], acc[b]);
+        const float4 a0 = *(const float4 *)wr, a1 = *(const float4 *)(wr + 4);
+        w[r][0] = a0.x; w[r][1] = a0.y; w[r][2] = a0.z; w[r][3] = a0.w;
+        w[r][4] = a1.x; w[r][5] = a1.y; w[r][6] = a1.z; w[r][7] = a1.w;
       }
     }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = wave_sum(acc[b]);
-    if (lane == 0) {
-      const float bv = bias ? to_f32(bias[n]) : 0.f;
+    for (int r = 0; r < GEMV_ROWS; ++r)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) g.y[prob][(int64_t)b * g.y_stride[prob] + n] = acc[b] + bv;
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][b] = fmaf(w[r][e], fx[b][c][e], acc[r][b]);
+  }
+#pragma unroll
+  for (int r = 0; r < GEMV_ROWS; ++r) {
+    const int n = row0 + r;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float v = wave_sum(acc[r][b]);
+      if (lane == 0 && n < N) g.y[prob][(int64_t)b * g.y_stride[prob] + n] = v + (bias ? to_f32(bias[n]) : 0.f);
     }
   }
 }
@@ -250,9 +275,9 @@ template <typename T, int NB>
 hipError_t gemv_run(const GemvBatch &g, const float *x, int K, bool silu_in, hipStream_t st) {
   int maxN = 0;
   for (int i = 0; i < g.nprob; ++i) maxN = g.N[i] > maxN ? g.N[i] : maxN;
-  const int rows_per_block = 4 * GEMV_ROWS_PER_WAVE;
+  const int rows_per_block = GEMV_WAVES * GEMV_ROWS;
   dim3 grid((maxN + rows_per_block - 1) / rows_per_block, g.nprob);
-  hipLaunchKernelGGL((gemv_kernel<T, NB>), grid, dim3(256), NB * K * sizeof(float), st, g, x, K, silu_in ? 1 : 0);
+  hipLaunchKernelGGL((gemv_kernel<T, NB>), grid, dim3(256), 0, st, g, x, K, silu_in ? 1 : 0);
   return hipGetLastError();
 }
 

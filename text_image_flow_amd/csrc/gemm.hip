@@ -151,7 +151,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmProblem &p, const f32x16 
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NSTAGE, int SWZ, int EPI>
+template <int BM, int BN, int WM, int WN, int NSTAGE, int SWZ, int EPI, int GM, bool XCD = true>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dma(GemmProblem p0, GemmProblem p1, int tiles0,
                                                               int ntm0, int ntm1, int total_tiles) {
   using namespace dma;
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dma(GemmProblem p0, Ge
   // XCD-aware order: dispatch round-robins workgroups over the 8 XCDs, so
   // give XCD x a contiguous run of logical tiles (sharing its L2).
   int bid = blockIdx.x;
-  {
+  if (XCD) {
     const int per = total_tiles / 8;
     if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
   }
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dma(GemmProblem p0, Ge
   const GemmProblem p = second ? p1 : p0;
   if (second) bid -= tiles0;
   const int ntm = second ? ntm1 : ntm0;
-  // grouped order: GM m-tiles vary fastest inside a group, then n
-  constexpr int GM = 8;
+  // grouped order: GM m-tiles vary fastest inside a group, then n, so the
+  // tiles an XCD runs together share GM panels of A and stream W panels
   const int ntn = (SWI ? p.N / (BN / 2) : p.N / BN);
   const int group = bid / (GM * ntn), first_m = group * GM;
   const int gsz = (ntm - first_m) < GM ? (ntm - first_m) : GM;
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void gemm_f32_simple(GemmProblem p0, GemmProbl
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NSTAGE, int SWZ, int EPI>
+template <int BM, int BN, int WM, int WN, int NSTAGE, int SWZ, int EPI, int GM = 4, bool XCD = true>
 hipError_t run_dma(const GemmProblem *pr, int np, hipStream_t st) {
   const int wn = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   int ntm[2] = {0, 0}, tiles[2] = {0, 0};
@@ -362,7 +362,7 @@ hipError_t run_dma(const GemmProblem *pr, int np, hipStream_t st) {
   const int total = tiles[0] + tiles[1];
   if (total == 0) return hipSuccess;
   GemmProblem q1 = np > 1 ? pr[1] : pr[0];
-  hipLaunchKernelGGL((gemm_bf16_dma<BM, BN, WM, WN, NSTAGE, SWZ, EPI>), dim3(total), dim3(64 * WM * WN), 0, st,
+  hipLaunchKernelGGL((gemm_bf16_dma<BM, BN, WM, WN, NSTAGE, SWZ, EPI, GM, XCD>), dim3(total), dim3(64 * WM * WN), 0, st,
                      pr[0], q1, tiles[0], ntm[0] > 0 ? ntm[0] : 1, ntm[1] > 0 ? ntm[1] : 1, total);
   return hipGetLastError();
 }
