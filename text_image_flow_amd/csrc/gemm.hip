@@ -5,15 +5,29 @@
 // to_out / to_add_out, img_mlp / txt_mlp w1 w3 w2 in the Lens-Turbo-3.8B-bf16
 // article; the gated residual and gated MLP of the Lens blog's "Overview").
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 (gfx950), fp32 accumulation.  A
-// workgroup of WM x WN waves computes a BM x BN tile (256 x 256 with 8
-// waves, two per SIMD, for the large projections).  K advances in slabs of
-// 32 that direct global->LDS loads drop into a ring of LDS stages, several
-// slabs ahead of the MFMAs.  Both operands are K-contiguous, so every load
-// and every LDS fragment read is a 16-byte vector.  The epilogue stages the
-// accumulators through LDS and writes rows with 16-byte stores.  Image and
-// text problems (different weights, different M) run in one grouped launch,
-// in an order that keeps each XCD's tiles on shared A and W panels.
+// bf16 path (gemm_bf16): v_mfma_f32_32x32x16_bf16 (gfx950), fp32
+// accumulation, one persistent workgroup per CU.
+//  * Tiles are BM x BN (256 x 256 for the large projections) computed by
+//    WM x WN waves.  Image and text problems (different weights and M, same
+//    N and K) share one launch; the tile order groups GM m-tiles so that the
+//    tiles an XCD runs together share A and W panels, and workgroup b (which
+//    the dispatcher places on XCD b % 8) walks a contiguous run of it.
+//  * K advances in slabs 64 deep, so every slab row is one whole 128-byte
+//    line: the address path serves a wave instruction covering 8 full lines
+//    much faster than one covering 16 half lines.  Direct global->LDS loads
+//    (each lane's 16 bytes land at M0 + 16 * lane; no VGPR holds staged data)
+//    fill two rings, three A stages and two W stages (160 KB).  Chunk c of
+//    row r sits in slot c ^ ((r >> 1) & 7), so any 16 consecutive rows of a
+//    fragment read hit all 64 banks.
+//  * The slab stream runs on across tile boundaries, so the next tile's first
+//    slabs load while this tile's epilogue runs.  Fragments are
+//    double-buffered (step ks + 1's LDS reads go out before step ks's
+//    MFMAs) and a slab's loads are spread over the four k steps.
+//  * The epilogue works from registers: the MFMAs take the weight fragment as
+//    the first operand, so each lane's accumulators hold one token and runs
+//    of 4 consecutive features (C^T layout); one permlane32 swap per dword
+//    makes 8 consecutive bf16 per lane for a 16-byte store.  Biases arrive
+//    through scalar loads, which leave the vector-memory counter to the slabs.
 //
 // fp32 path: a plain LDS-tiled FMA kernel with the same epilogues, used by
 // the fp32 configuration (correctness, not speed).
@@ -47,19 +61,13 @@ __device__ __forceinline__ void epi_swiglu(const GemmProblem &p, int m, int n, f
   ((T *)p.C)[(int64_t)m * p.N + n] = from_f32<T>(silu_f(g) * u);
 }
 
-// ------------------------------------------- bf16 MFMA, LDS-DMA pipeline
-// Direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
-// land at M0 + 16 * lane, so one wave instruction fills 1 KB of LDS) into a
-// ring of NSTAGE slabs of BK = 32, prefetching NSTAGE - 1 slabs ahead; no
-// VGPRs hold staged data.  A slab row is 64 bytes (four 16-byte chunks); the
-// chunk of row r at k-chunk c sits in slot c ^ ((r >> SWZ_SHIFT) & 3), which
-// spreads the 32 rows one fragment read touches over all LDS banks.
-namespace dma {
-constexpr int DBK = 32;            // k per slab
-constexpr int ROWB = DBK * 2;      // bytes per slab row
+namespace gk {
+constexpr int RBK = 64;            // k per slab
+constexpr int RROW = RBK * 2;      // bytes per slab row (one 128-byte line)
 typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(4))) unsigned *cptr;
 
-__device__ __forceinline__ int swz(int r, int shift) { return (r >> shift) & 3; }
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
 template <int N>
@@ -69,178 +77,168 @@ __device__ __forceinline__ void wait_vm() {
 }
 // lgkmcnt(0) only: this wave's LDS reads have returned
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
-}  // namespace dma
 
-// Epilogue through LDS, one wm-slice (WTM rows) at a time: the waves of
-// that slice park their fp32 accumulators in row-major order, then every
-// thread applies the epilogue to 8 consecutive columns and writes them with
-// 16-byte vector stores.  bcol[j]: tile column of accumulator tile j for
-// this lane.  st must hold WTM * (BN + 4) floats; the caller's LDS is free.
-template <int BM, int BN, int WM, int MT, int NT, int NTH, int EPI>
-__device__ __forceinline__ void epilogue_lds(const GemmProblem &p, const f32x16 (&acc)[MT][NT], float *st, int m0,
-                                             int n0, int wm, const int (&bcol)[NT], int lane, int tid) {
-  constexpr int WTM = BM / WM;
-  constexpr int EPI_LDW = BN + 4;
-  constexpr bool SWI = (EPI == EPI_SWIGLU);
-  const int M = p.M;
-  const int rh = (lane >> 5) * 4;
-#pragma unroll
-  for (int h = 0; h < WM; ++h) {
-    dma::wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    if (wm == h) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            st[(i * 32 + (r >> 2) * 8 + rh + (r & 3)) * EPI_LDW + bcol[j]] = acc[i][j][r];
-    }
-    dma::wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    constexpr int OUTC = SWI ? BN / 2 : BN;      // output columns of the tile
-    constexpr int TPR = OUTC / 8;                // threads per row
-    constexpr int RPP = NTH / TPR;               // rows per pass
-    const int c8 = (tid % TPR) * 8;
-    const int n = n0 + c8;
-    for (int rr = tid / TPR; rr < WTM; rr += RPP) {
-      const int m = m0 + h * WTM + rr;
-      if (m >= M) break;
-      const float *src = st + rr * EPI_LDW + c8;
-      float v[8];
-      *(float4 *)&v[0] = *(const float4 *)src;
-      *(float4 *)&v[4] = *(const float4 *)(src + 4);
-      if constexpr (SWI) {
-        float u[8];
-        *(float4 *)&u[0] = *(const float4 *)(src + BN / 2);
-        *(float4 *)&u[4] = *(const float4 *)(src + BN / 2 + 4);
-        bf16x8 o;
-        const bf16x8 b1 = p.bias ? *(const bf16x8 *)((const bf16 *)p.bias + n) : bf16x8{};
-        const bf16x8 b3 = p.bias3 ? *(const bf16x8 *)((const bf16 *)p.bias3 + n) : bf16x8{};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (bf16)(silu_f(v[e] + (float)b1[e]) * (u[e] + (float)b3[e]));
-        *(bf16x8 *)((bf16 *)p.C + (int64_t)m * p.N + n) = o;
-      } else {
-        if (p.bias) {
-          const bf16x8 bb = *(const bf16x8 *)((const bf16 *)p.bias + n);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += (float)bb[e];
-        }
-        if constexpr (EPI == EPI_STORE) {
-          bf16x8 o;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
-          *(bf16x8 *)((bf16 *)p.C + (int64_t)m * p.N + n) = o;
-        } else if constexpr (EPI == EPI_STORE_F32) {
-          float *dst = (float *)p.C + (int64_t)m * p.N + n;
-          *(float4 *)dst = *(float4 *)&v[0];
-          *(float4 *)(dst + 4) = *(float4 *)&v[4];
-        } else {
-          const float *g = p.gate + (int64_t)(m / p.rows_per_gate) * p.gate_stride + n;
-          float *dst = (float *)p.C + (int64_t)m * p.N + n;
-          float4 h0 = *(float4 *)dst, h1 = *(float4 *)(dst + 4);
-          const float4 g0 = *(const float4 *)g, g1 = *(const float4 *)(g + 4);
-          h0.x += g0.x * v[0]; h0.y += g0.y * v[1]; h0.z += g0.z * v[2]; h0.w += g0.w * v[3];
-          h1.x += g1.x * v[4]; h1.y += g1.y * v[5]; h1.z += g1.z * v[6]; h1.w += g1.w * v[7];
-          *(float4 *)dst = h0;
-          *(float4 *)(dst + 4) = h1;
-        }
-      }
-    }
-  }
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ unsigned pack_bf2(float a, float b) {
+  const bf16x2 t = {(bf16)a, (bf16)b};
+  return __builtin_bit_cast(unsigned, t);
 }
 
-template <int BM, int BN, int WM, int WN, int NSTAGE, int SWZ, int EPI, int GM, bool XCD = true>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dma(GemmProblem p0, GemmProblem p1, int tiles0,
-                                                              int ntm0, int ntm1, int total_tiles) {
-  using namespace dma;
-  constexpr int NTH = 64 * WM * WN, NW = WM * WN;
+// Tile t of the grouped launch -> problem (second), first row and column.
+__device__ __forceinline__ void tile_coords(int t, int tiles0, int ntm0, int ntm1, int ntn, int gm, int bm, int outc,
+                                            bool &second, int &m0, int &n0) {
+  second = t >= tiles0;
+  const int b = second ? t - tiles0 : t;
+  const int ntm = second ? ntm1 : ntm0;
+  const int group = b / (gm * ntn), first_m = group * gm;
+  const int gsz = (ntm - first_m) < gm ? (ntm - first_m) : gm;
+  const int r = b % (gm * ntn);
+  m0 = (first_m + r % gsz) * bm;
+  n0 = (r / gsz) * outc;
+}
+
+// Two runs of 4 accumulators as bf16 pairs (features 8q .. 8q+3 on lanes
+// 0-31 and 8q+4 .. 8q+7 on lanes 32-63, then the same for q+1): after the
+// swaps lanes 0-31 hold features 8q .. 8q+7 and lanes 32-63 8q+8 .. 8q+15.
+__device__ __forceinline__ u32x4 pair_runs(unsigned x0, unsigned x1, unsigned y0, unsigned y1) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+  return u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+}  // namespace gk
+
+template <int BM, int BN, int WM, int WN, int EPI, int GM>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmProblem p1, int tiles0, int ntm0,
+                                                          int ntm1, int total_tiles, int per_xcd) {
+  using namespace gk;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
   constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr int OUTC = SWI ? BN / 2 : BN;
+  constexpr int H = SWI ? NT / 2 : NT;          // output sub-tiles per wave along n
   static_assert(!SWI || NT % 2 == 0, "SwiGLU needs an even number of n tiles per wave");
-  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
-  // rows written by one wave instruction: 1 KB / 64 B = 16; per round of all waves: 16 * NW
-  constexpr int ROWS_PER_ROUND = 16 * NW;
-  constexpr int A_RND = BM / ROWS_PER_ROUND, B_RND = BN / ROWS_PER_ROUND;
-  static_assert(A_RND * ROWS_PER_ROUND == BM && B_RND * ROWS_PER_ROUND == BN, "rows must split over waves");
-  constexpr int LD_PER_STAGE = A_RND + B_RND;   // load instructions per thread per slab
-  constexpr int EPI_LDW = BN + 4;                // fp32 row stride of the epilogue staging
-  constexpr int EPI_BYTES = WTM * EPI_LDW * 4;
-  constexpr int SMEM = NSTAGE * STAGE > EPI_BYTES ? NSTAGE * STAGE : EPI_BYTES;
+  constexpr int NA = 3, NB = 2;                 // ring depths: A two slabs ahead, W one
+  constexpr int A_UNIT = BM * RROW, B_UNIT = BN * RROW;
+  constexpr int ROWS_PER_ROUND = 8 * NW;        // one wave instruction: 8 rows x 128 B
+  constexpr int LDA = BM / ROWS_PER_ROUND, LDB = BN / ROWS_PER_ROUND;
+  static_assert(LDA * ROWS_PER_ROUND == BM && LDB * ROWS_PER_ROUND == BN, "rows must split over waves");
+  constexpr int KS = RBK / 16;                  // MFMA k steps per slab
+  static_assert(LDB % (KS / 2) == 0 && LDA % (KS / 2) == 0, "load parts must split over half the steps");
+  constexpr int PB = LDB / (KS / 2), PA = LDA / (KS / 2);
+  constexpr int SMEM = NA * A_UNIT + NB * B_UNIT;
+  static_assert(SMEM <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  char *const a_ring = smem;
+  char *const b_ring = smem + NA * A_UNIT;
 
-  // XCD-aware order: dispatch round-robins workgroups over the 8 XCDs, so
-  // give XCD x a contiguous run of logical tiles (sharing its L2).
-  int bid = blockIdx.x;
-  if (XCD) {
-    const int per = total_tiles / 8;
-    if (bid < per * 8) bid = (bid % 8) * per + bid / 8;
-  }
-  const bool second = bid >= tiles0;
-  const GemmProblem p = second ? p1 : p0;
-  if (second) bid -= tiles0;
-  const int ntm = second ? ntm1 : ntm0;
-  // grouped order: GM m-tiles vary fastest inside a group, then n, so the
-  // tiles an XCD runs together share GM panels of A and stream W panels
-  const int ntn = (SWI ? p.N / (BN / 2) : p.N / BN);
-  const int group = bid / (GM * ntn), first_m = group * GM;
-  const int gsz = (ntm - first_m) < GM ? (ntm - first_m) : GM;
-  const int tm = first_m + (bid % (GM * ntn)) % gsz;
-  const int tn = (bid % (GM * ntn)) / gsz;
-  const int m0 = tm * BM;
-  const int n0 = tn * (SWI ? BN / 2 : BN);
+  // workgroup b sits on XCD b % 8; the XCD's tiles are one contiguous run
+  // of the grouped order, dealt round-robin to its workgroups
+  const int xcd = blockIdx.x & 7, nslot = gridDim.x >> 3;
+  const int t_end = min((xcd + 1) * per_xcd, total_tiles);
+  const int t_first = xcd * per_xcd + (blockIdx.x >> 3);
+  if (t_first >= t_end) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
-  const int M = p.M, K = p.K;
-  const bf16 *A = (const bf16 *)p.A;
-  const bf16 *W = (const bf16 *)p.W;
-  const bf16 *W3 = (const bf16 *)p.W3;
+  const int ntn = p0.N / OUTC;
+  const int K = p0.K, KT = K / RBK;
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const int dst0 = wave * 8 * RROW;             // wave's rows inside a round
 
-  // this lane's source rows/chunks for each load instruction of a slab
-  const int lrow = lane >> 2, lslot = lane & 3;
-  const bf16 *a_src[A_RND];
-  const bf16 *b_src[B_RND];
-#pragma unroll
-  for (int i = 0; i < A_RND; ++i) {
-    const int r = i * ROWS_PER_ROUND + wave * 16 + lrow;
-    int gr = m0 + r;
-    gr = gr < M ? gr : M - 1;
-    a_src[i] = A + (int64_t)gr * K + (lslot ^ swz(r, SWZ)) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_RND; ++i) {
-    const int r = i * ROWS_PER_ROUND + wave * 16 + lrow;
-    const bf16 *base;
-    if constexpr (SWI) {
-      base = r < BN / 2 ? W + (int64_t)(n0 + r) * K : W3 + (int64_t)(n0 + r - BN / 2) * K;
-    } else {
-      base = W + (int64_t)(n0 + r) * K;
-    }
-    b_src[i] = base + (lslot ^ swz(r, SWZ)) * 8;
-  }
-  // LDS destination (wave-uniform) of instruction i inside a stage
-  const int a_dst0 = wave * 16 * ROWB, b_dst0 = A_BYTES + wave * 16 * ROWB;
-
-#define DMA_ISSUE(kt_)                                                                                   \
-  do {                                                                                                   \
-    char *sb_ = smem + ((kt_) % NSTAGE) * STAGE;                                                         \
-    const int k0_ = (kt_) * DBK;                                                                         \
-    _Pragma("unroll") for (int i = 0; i < A_RND; ++i) __builtin_amdgcn_global_load_lds(                  \
-        (const void *)(a_src[i] + k0_), (lds_void *)(sb_ + a_dst0 + i * ROWS_PER_ROUND * ROWB), 16, 0, 0); \
-    _Pragma("unroll") for (int i = 0; i < B_RND; ++i) __builtin_amdgcn_global_load_lds(                  \
-        (const void *)(b_src[i] + k0_), (lds_void *)(sb_ + b_dst0 + i * ROWS_PER_ROUND * ROWB), 16, 0, 0); \
+  // ---- two load streams (A and W), each with its own tile / slab cursor
+  const bf16 *a_src[LDA];
+  const bf16 *b_src[LDB];
+  int at = t_first, akt = 0, apos = 0;
+  int bt = t_first, bkt = 0, bpos = 0;
+#define A_SETUP(t_)                                                                                       \
+  do {                                                                                                    \
+    bool sec_;                                                                                            \
+    int m0_, n0_;                                                                                         \
+    tile_coords(t_, tiles0, ntm0, ntm1, ntn, GM, BM, OUTC, sec_, m0_, n0_);                               \
+    const bf16 *A_ = (const bf16 *)(sec_ ? p1.A : p0.A);                                                  \
+    const int M_ = sec_ ? p1.M : p0.M;                                                                    \
+    _Pragma("unroll") for (int i = 0; i < LDA; ++i) {                                                     \
+      const int r = i * ROWS_PER_ROUND + wave * 8 + lrow;                                                 \
+      const int gr = m0_ + r < M_ ? m0_ + r : M_ - 1;                                                     \
+      a_src[i] = A_ + (int64_t)gr * K + (lslot ^ swz(r)) * 8;                                             \
+    }                                                                                                     \
+  } while (0)
+#define B_SETUP(t_)                                                                                       \
+  do {                                                                                                    \
+    bool sec_;                                                                                            \
+    int m0_, n0_;                                                                                         \
+    tile_coords(t_, tiles0, ntm0, ntm1, ntn, GM, BM, OUTC, sec_, m0_, n0_);                               \
+    const bf16 *W_ = (const bf16 *)(sec_ ? p1.W : p0.W);                                                  \
+    const bf16 *W3_ = (const bf16 *)(sec_ ? p1.W3 : p0.W3);                                               \
+    _Pragma("unroll") for (int i = 0; i < LDB; ++i) {                                                     \
+      const int r = i * ROWS_PER_ROUND + wave * 8 + lrow;                                                 \
+      const bf16 *base_;                                                                                  \
+      if constexpr (SWI) {                                                                                \
+        base_ = r < BN / 2 ? W_ + (int64_t)(n0_ + r) * K : W3_ + (int64_t)(n0_ + r - BN / 2) * K;         \
+      } else {                                                                                            \
+        base_ = W_ + (int64_t)(n0_ + r) * K;                                                              \
+      }                                                                                                   \
+      b_src[i] = base_ + (lslot ^ swz(r)) * 8;                                                            \
+    }                                                                                                     \
+  } while (0)
+// one load instruction (part i) of the current A / W slab, and the cursor
+// step once all parts of the slab are out
+#define ISSUE_A_PART(i_)                                                                                   \
+  __builtin_amdgcn_global_load_lds((const void *)(a_src[i_] + akt * RBK),                                  \
+                                   (lds_void *)(a_ring + apos * A_UNIT + dst0 + (i_) * ROWS_PER_ROUND * RROW), \
+                                   16, 0, 0)
+#define ISSUE_B_PART(i_)                                                                                   \
+  __builtin_amdgcn_global_load_lds((const void *)(b_src[i_] + bkt * RBK),                                  \
+                                   (lds_void *)(b_ring + bpos * B_UNIT + dst0 + (i_) * ROWS_PER_ROUND * RROW), \
+                                   16, 0, 0)
+#define STEP_A()                                                                                           \
+  do {                                                                                                     \
+    apos = apos + 1 == NA ? 0 : apos + 1;                                                                  \
+    ++a_issued;                                                                                            \
+    if (++akt == KT) {                                                                                     \
+      akt = 0;                                                                                             \
+      at += nslot;                                                                                         \
+      if (at < t_end) A_SETUP(at);                                                                         \
+    }                                                                                                      \
+  } while (0)
+#define STEP_B()                                                                                           \
+  do {                                                                                                     \
+    bpos = bpos + 1 == NB ? 0 : bpos + 1;                                                                  \
+    if (++bkt == KT) {                                                                                     \
+      bkt = 0;                                                                                             \
+      bt += nslot;                                                                                         \
+      if (bt < t_end) B_SETUP(bt);                                                                         \
+    }                                                                                                      \
+  } while (0)
+#define ISSUE_A()                                                                                          \
+  do {                                                                                                     \
+    if (at < t_end) {                                                                                      \
+      _Pragma("unroll") for (int i = 0; i < LDA; ++i) ISSUE_A_PART(i);                                     \
+      STEP_A();                                                                                            \
+    }                                                                                                      \
+  } while (0)
+#define ISSUE_B()                                                                                          \
+  do {                                                                                                     \
+    if (bt < t_end) {                                                                                      \
+      _Pragma("unroll") for (int i = 0; i < LDB; ++i) ISSUE_B_PART(i);                                     \
+      STEP_B();                                                                                            \
+    }                                                                                                      \
   } while (0)
 
-  f32x16 acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
+  // Issue order: A0 W0 A1, then in iteration k W(k+1) and after it A(k+2).
+  // So when slab k is computed, W(k) is the newest W slab issued and at most
+  // A(k+1) followed it (epilogue stores in between only make the wait
+  // stricter).
+  int a_issued = 0, consumed = 0;
+  A_SETUP(at);
+  B_SETUP(bt);
+  ISSUE_A();
+  ISSUE_B();
+  ISSUE_A();
 
-  // fragment rows for this lane
   const int frow = lane & 31, hl = lane >> 5;
   int a_row[MT], b_row[NT];
 #pragma unroll
@@ -248,53 +246,222 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dma(GemmProblem p0, Ge
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     if constexpr (SWI) {
-      constexpr int H = NT / 2;
       b_row[j] = (j < H ? wn * (WTN / 2) + j * 32 : BN / 2 + wn * (WTN / 2) + (j - H) * 32) + frow;
     } else {
       b_row[j] = wn * WTN + j * 32 + frow;
     }
   }
+  int ca = 0, cb = 0;                           // ring positions of the slab being computed
 
-  const int KT = K / DBK;
+  for (int ct = t_first; ct < t_end; ct += nslot) {
+    f32x16 acc[MT][NT];
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < KT) DMA_ISSUE(s);
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
 
-  for (int kt = 0; kt < KT; ++kt) {
-    // slabs issued after kt that may stay in flight
-    const int ahead = (KT - 1 - kt) < (NSTAGE - 2) ? (KT - 1 - kt) : (NSTAGE - 2);
-    if (ahead >= 2) wait_vm<2 * LD_PER_STAGE>();
-    else if (ahead == 1) wait_vm<LD_PER_STAGE>();
-    else wait_vm<0>();
-    // Barrier without a memory fence: the waits above cover this wave's
-    // slab loads and LDS reads, and a fence would drain every prefetch.
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    if (kt + NSTAGE - 1 < KT) DMA_ISSUE(kt + NSTAGE - 1);
-    const char *sb = smem + (kt % NSTAGE) * STAGE;
+    for (int kt = 0; kt < KT; ++kt) {
+      if (a_issued > consumed + 1) wait_vm<LDA>();
+      else wait_vm<0>();
+      // Barrier without a memory fence: the wait covers this wave's slab
+      // loads, and every wave is done with the slots about to be refilled.
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+
+      // This iteration's loads, spread over the k steps with all W parts
+      // before any A part (which keeps "only A(k + 1) follows W(k)" true).
+      const bool do_b = bt < t_end, do_a = at < t_end;
+      const char *sa = a_ring + ca * A_UNIT;
+      const char *sb = b_ring + cb * B_UNIT;
+      bf16x8 fa[2][MT], fb[2][NT];
+#define READ_FRAGS(buf_, ks_)                                                                              \
+  do {                                                                                                     \
+    const int c_ = (ks_) * 2 + hl;                                                                         \
+    _Pragma("unroll") for (int i = 0; i < MT; ++i) fa[buf_][i] =                                          \
+        *(const bf16x8 *)(sa + a_row[i] * RROW + ((c_ ^ swz(a_row[i])) << 4));                            \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j) fb[buf_][j] =                                          \
+        *(const bf16x8 *)(sb + b_row[j] * RROW + ((c_ ^ swz(b_row[j])) << 4));                            \
+  } while (0)
+      READ_FRAGS(0, 0);
 #pragma unroll
-    for (int ks = 0; ks < DBK / 16; ++ks) {
-      const int c = ks * 2 + hl;   // 16-byte k-chunk this lane reads
-      bf16x8 fa[MT], fb[NT];
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < KS) READ_FRAGS(cur ^ 1, ks + 1);
+        if (ks < KS / 2) {
+          if (do_b) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        fa[i] = *(const bf16x8 *)(sb + a_row[i] * ROWB + ((c ^ swz(a_row[i], SWZ)) << 4));
+            for (int i = ks * PB; i < (ks + 1) * PB; ++i) ISSUE_B_PART(i);
+          }
+        } else {
+          if (do_a) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        fb[j] = *(const bf16x8 *)(sb + A_BYTES + b_row[j] * ROWB + ((c ^ swz(b_row[j], SWZ)) << 4));
+            for (int i = (ks - KS / 2) * PA; i < (ks - KS / 2 + 1) * PA; ++i) ISSUE_A_PART(i);
+          }
+        }
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < NT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+      }
+#undef READ_FRAGS
+      if (do_b) STEP_B();
+      if (do_a) STEP_A();
+      ca = ca + 1 == NA ? 0 : ca + 1;
+      cb = cb + 1 == NB ? 0 : cb + 1;
+      ++consumed;
     }
-  }
 
-#undef DMA_ISSUE
-  int bcol[NT];
+    // ---- epilogue from registers
+    bool sec;
+    int m0, n0;
+    tile_coords(ct, tiles0, ntm0, ntm1, ntn, GM, BM, OUTC, sec, m0, n0);
+    const int M = sec ? p1.M : p0.M, N = p0.N;
+    void *C = sec ? p1.C : p0.C;
+    const void *bias = sec ? p1.bias : p0.bias;
+    // wave's first output feature; lane holds features fw + j*32 + 8q + 4*hl + e
+    const int fw = n0 + wn * (WTN / (SWI ? 2 : 1));
+    const void *bias3 = SWI ? (sec ? p1.bias3 : p0.bias3) : nullptr;
+    // Biases of one 32-feature column group (16 dwords) per scalar load;
+    // this lane's 4 bf16 for (j, q) are dwords 4q + 2*hl + {0, 1}.
+#define LOAD_BIAS16(ptr_, j_, arr_)                                                        \
+  do {                                                                                     \
+    if (ptr_) {                                                                            \
+      const cptr bp_ = (cptr)((const bf16 *)(ptr_) + fw + (j_) * 32);                      \
+      _Pragma("unroll") for (int k = 0; k < 16; ++k) arr_[k] = bp_[k];                     \
+    } else {                                                                               \
+      _Pragma("unroll") for (int k = 0; k < 16; ++k) arr_[k] = 0;                          \
+    }                                                                                      \
+  } while (0)
+#define BIAS4(arr_, j_, q_, out_)                                                          \
+  do {                                                                                     \
+    const unsigned lo_ = hl ? arr_[4 * (q_) + 2] : arr_[4 * (q_)];                         \
+    const unsigned hi_ = hl ? arr_[4 * (q_) + 3] : arr_[4 * (q_) + 1];                     \
+    out_[0] = bf_lo(lo_);                                                            \
+    out_[1] = bf_hi(lo_);                                                            \
+    out_[2] = bf_lo(hi_);                                                            \
+    out_[3] = bf_hi(hi_);                                                            \
+  } while (0)
+    const float *gate_row = nullptr;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) bcol[j] = b_row[j] - frow + (lane & 31);
-  epilogue_lds<BM, BN, WM, MT, NT, NTH, EPI>(p, acc, (float *)smem, m0, n0, wm, bcol, lane, tid);
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + wm * WTM + i * 32 + frow;
+      const bool ok = m < M;
+      if constexpr (EPI == EPI_GATED) {
+        const GemmProblem &pg = p0;   // gate layout is shared by both problems
+        const float *g = sec ? p1.gate : pg.gate;
+        const int rpg = sec ? p1.rows_per_gate : p0.rows_per_gate;
+        const int gst = sec ? p1.gate_stride : p0.gate_stride;
+        gate_row = g + (int64_t)((ok ? m : 0) / rpg) * gst;
+      }
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const int f0 = fw + j * 32 + 4 * hl;     // + 8q
+        unsigned bw[16], bw3[16];
+        LOAD_BIAS16(bias, j, bw);
+        if constexpr (SWI) LOAD_BIAS16(bias3, j, bw3);
+        if constexpr (EPI == EPI_STORE || EPI == EPI_SWIGLU) {
+          unsigned pk[4][2];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float b[4], y[4];
+            BIAS4(bw, j, q, b);
+            if constexpr (SWI) {
+              float b3[4];
+              BIAS4(bw3, j, q, b3);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                y[e] = silu_f(acc[i][j][4 * q + e] + b[e]) * (acc[i][j + H][4 * q + e] + b3[e]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q + e] + b[e];
+            }
+            pk[q][0] = pack_bf2(y[0], y[1]);
+            pk[q][1] = pack_bf2(y[2], y[3]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; q += 2) {
+            const u32x4 o = pair_runs(pk[q][0], pk[q][1], pk[q + 1][0], pk[q + 1][1]);
+            if (ok) *(u32x4 *)((bf16 *)C + (int64_t)m * N + (f0 - 4 * hl) + 8 * q + 8 * hl) = o;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float b[4];
+            BIAS4(bw, j, q, b);
+            float4 y;
+            y.x = acc[i][j][4 * q + 0] + b[0];
+            y.y = acc[i][j][4 * q + 1] + b[1];
+            y.z = acc[i][j][4 * q + 2] + b[2];
+            y.w = acc[i][j][4 * q + 3] + b[3];
+            float *dst = (float *)C + (int64_t)m * N + f0 + 8 * q;
+            if constexpr (EPI == EPI_STORE_F32) {
+              if (ok) *(float4 *)dst = y;
+            } else {
+              if (ok) {
+                const float4 g4 = *(const float4 *)(gate_row + f0 + 8 * q);
+                float4 h4 = *(float4 *)dst;
+                h4.x += g4.x * y.x;
+                h4.y += g4.y * y.y;
+                h4.z += g4.z * y.z;
+                h4.w += g4.w * y.w;
+                *(float4 *)dst = h4;
+              }
+            }
+          }
+        }
+      }
+    }
+#undef BIAS4
+#undef LOAD_BIAS16
+  }
+#undef ISSUE_A
+#undef ISSUE_B
+#undef ISSUE_A_PART
+#undef ISSUE_B_PART
+#undef STEP_A
+#undef STEP_B
+#undef A_SETUP
+#undef B_SETUP
+}
+
+// Persistent launch: at most one workgroup per CU, a multiple of 8 so that
+// every XCD gets the same number of workgroups.
+int cu_count() {
+  static int n[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 256;
+  if (n[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    n[dev] = c;
+  }
+  return n[dev];
+}
+
+// Both problems of a grouped launch must share N and K (the image and text
+// weights of one layer do); N must be a multiple of the tile's output
+// columns and K of the slab depth.
+template <int BM, int BN, int WM, int WN, int EPI, int GM = 4>
+hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st) {
+  const int outc = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  if (np > 1 && (pr[0].N != pr[1].N || pr[0].K != pr[1].K)) return hipErrorInvalidValue;
+  if (pr[0].N % outc || pr[0].K % gk::RBK || pr[0].K <= 0) return hipErrorInvalidValue;
+  int ntm[2] = {0, 0}, tiles[2] = {0, 0};
+  for (int i = 0; i < np; ++i) {
+    ntm[i] = (pr[i].M + BM - 1) / BM;
+    tiles[i] = pr[i].M > 0 ? ntm[i] * (pr[i].N / outc) : 0;
+  }
+  const int total = tiles[0] + tiles[1];
+  if (total == 0) return hipSuccess;
+  const int per_xcd = (total + 7) / 8;
+  int grid = cu_count() / 8 * 8;
+  if (grid > per_xcd * 8) grid = per_xcd * 8;
+  GemmProblem q0 = pr[0], q1 = np > 1 ? pr[1] : pr[0];
+  if (tiles[0] == 0) q0 = q1;
+  hipLaunchKernelGGL((gemm_bf16<BM, BN, WM, WN, EPI, GM>), dim3(grid), dim3(64 * WM * WN), 0, st, q0, q1, tiles[0],
+                     ntm[0] > 0 ? ntm[0] : 1, ntm[1] > 0 ? ntm[1] : 1, total, per_xcd);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ fp32 (FMA)
@@ -351,22 +518,6 @@ __global__ __launch_bounds__(256) void gemm_f32_simple(GemmProblem p0, GemmProbl
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NSTAGE, int SWZ, int EPI, int GM = 4, bool XCD = true>
-hipError_t run_dma(const GemmProblem *pr, int np, hipStream_t st) {
-  const int wn = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  int ntm[2] = {0, 0}, tiles[2] = {0, 0};
-  for (int i = 0; i < np; ++i) {
-    ntm[i] = (pr[i].M + BM - 1) / BM;
-    tiles[i] = pr[i].M > 0 ? ntm[i] * (pr[i].N / wn) : 0;
-  }
-  const int total = tiles[0] + tiles[1];
-  if (total == 0) return hipSuccess;
-  GemmProblem q1 = np > 1 ? pr[1] : pr[0];
-  hipLaunchKernelGGL((gemm_bf16_dma<BM, BN, WM, WN, NSTAGE, SWZ, EPI, GM, XCD>), dim3(total), dim3(64 * WM * WN), 0, st,
-                     pr[0], q1, tiles[0], ntm[0] > 0 ? ntm[0] : 1, ntm[1] > 0 ? ntm[1] : 1, total);
-  return hipGetLastError();
-}
-
 template <int EPI>
 hipError_t run_f32(const GemmProblem *pr, int np, hipStream_t st) {
   int ntm[2] = {1, 1}, tiles[2] = {0, 0};
@@ -384,11 +535,9 @@ hipError_t run_f32(const GemmProblem *pr, int np, hipStream_t st) {
 
 }  // namespace
 
-// bf16 tile choice: 256 x 256 tiles (8 waves, 2 per SIMD) unless that grid
-// would leave the chip under-filled, then 128 x 256 tiles; N not a
-// multiple of 256 (the 128-wide velocity projection) takes 256 x 128.
-// The caller guarantees K % 32 == 0 and N % 128 == 0 (SwiGLU: N % 128 == 0
-// output columns, i.e. 256 rows of w1 | w3 per tile).  M may be anything.
+// bf16 tile choice: 256 x 256 tiles, or 128 x 256 when those would leave
+// most CUs idle, or 256 x 128 when N is not a multiple of 256 (N = 128
+// for the final projection).
 template <int EPI>
 hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st) {
   constexpr bool SWI = EPI == EPI_SWIGLU;
@@ -399,10 +548,12 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st) {
     if (pr[i].N % outc) n256 = false;
     tiles256 += ((pr[i].M + 255) / 256) * (pr[i].N / outc);
   }
-  if (!n256) return run_dma<256, 128, 4, 2, 4, 2, EPI>(pr, np, st);
-  if (tiles256 < 200) return run_dma<128, 256, 2, 4, 4, 2, EPI>(pr, np, st);
-  if (SWI) return run_dma<256, 256, 2, 4, 3, 2, EPI>(pr, np, st);
-  return run_dma<256, 256, 2, 4, 4, 2, EPI>(pr, np, st);
+  if (!n256) {
+    if constexpr (SWI) return hipErrorInvalidValue;
+    else return run_bf16<256, 128, 4, 2, EPI>(pr, np, st);
+  }
+  if (tiles256 * 2 < cu_count()) return run_bf16<128, 256, 2, 4, EPI>(pr, np, st);
+  return run_bf16<256, 256, 2, 4, EPI>(pr, np, st);
 }
 
 hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream) {
