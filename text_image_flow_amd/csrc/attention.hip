@@ -72,7 +72,9 @@ constexpr float TAU = 8.0f;
 // global->LDS loads (global_load_lds_dwordx4: one wave instruction fills 1 KB
 // = 8 rows of 128 bytes) into a double-buffered ring, so no VGPRs stage
 // them.  Rows are unpadded; 16-byte chunk c of row r sits in slot
-// c ^ (r & 7), which spreads the 32 rows of a fragment read over the banks.
+// c ^ ((r >> 1) & 7): the 16 lanes that one LDS cycle serves read 16
+// consecutive rows, and these land on 16 distinct 16-byte bank groups of the
+// 64 banks (a plain c ^ (r & 7) maps rows r and r + 8 onto the same group).
 // The partial last tile is peeled so the steady-state loop carries no mask.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -89,7 +91,7 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
                                              float &m_run, float &l_run, f32x16 &minit, int kv0, int n_kv, int ql,
                                              int hl) {
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  const int sw = ql & 7;   // rows ql and 32 + ql share the swizzle
+  const int sw = (ql >> 1) & 7;   // rows ql and 32 + ql share the swizzle
   f32x16 s0, s1;
   {
     const int slot = (hl ^ sw) << 4;
@@ -202,10 +204,10 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   // each wave fills rows [wave * 16, wave * 16 + 16) of the K and V^T tiles:
   // two instructions of 8 rows each; lane -> row + lane / 8, slot lane % 8
   const int r0 = wave * 16 + (lane >> 3), r1 = r0 + 8, slot = lane & 7;
-  const bf16 *k_src0 = Kg + (int64_t)r0 * 64 + ((slot ^ (r0 & 7)) * 8);
-  const bf16 *k_src1 = Kg + (int64_t)r1 * 64 + ((slot ^ (r1 & 7)) * 8);
-  const bf16 *v_src0 = Vg + (int64_t)r0 * a.S_pad + ((slot ^ (r0 & 7)) * 8);
-  const bf16 *v_src1 = Vg + (int64_t)r1 * a.S_pad + ((slot ^ (r1 & 7)) * 8);
+  const bf16 *k_src0 = Kg + (int64_t)r0 * 64 + ((slot ^ ((r0 >> 1) & 7)) * 8);
+  const bf16 *k_src1 = Kg + (int64_t)r1 * 64 + ((slot ^ ((r1 >> 1) & 7)) * 8);
+  const bf16 *v_src0 = Vg + (int64_t)r0 * a.S_pad + ((slot ^ ((r0 >> 1) & 7)) * 8);
+  const bf16 *v_src1 = Vg + (int64_t)r1 * a.S_pad + ((slot ^ ((r1 >> 1) & 7)) * 8);
   const int dst0 = wave * 16 * 128, dst1 = dst0 + 8 * 128;
 #define ATT_ISSUE(t_)                                                                                       \
   do {                                                                                                      \

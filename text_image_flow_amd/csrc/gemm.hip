@@ -16,7 +16,11 @@
 //    line: the address path serves a wave instruction covering 8 full lines
 //    much faster than one covering 16 half lines.  Direct global->LDS loads
 //    (each lane's 16 bytes land at M0 + 16 * lane; no VGPR holds staged data)
-//    fill two rings, three A stages and two W stages (160 KB).  Chunk c of
+//    fill two rings, three A stages and two W stages (160 KB).  They are raw
+//    buffer loads (buffer_load_dwordx4 ... lds): each lane keeps one 32-bit
+//    row offset and the slab's k offset rides in the scalar offset, so a
+//    load needs no address arithmetic (64-bit global loads are the fallback
+//    for operands of 2 GiB or more).  Chunk c of
 //    row r sits in slot c ^ ((r >> 1) & 7), so any 16 consecutive rows of a
 //    fragment read hit all 64 banks.
 //  * The slab stream runs on across tile boundaries, so the next tile's first
@@ -75,6 +79,12 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+// 16 bytes per lane from base + voff + soff into LDS at M0 + 16 * lane, as a
+// raw buffer load (bounds = bytes)
+__device__ __forceinline__ void buffer_lds16(const void *base, int bytes, lds_void *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, bytes, 0x00020000),
+                                           dst, 16, voff, soff, 0, 0);
+}
 // lgkmcnt(0) only: this wave's LDS reads have returned
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
@@ -108,7 +118,7 @@ __device__ __forceinline__ u32x4 pair_runs(unsigned x0, unsigned x1, unsigned y0
 }
 }  // namespace gk
 
-template <int BM, int BN, int WM, int WN, int EPI, int GM>
+template <int BM, int BN, int WM, int WN, int EPI, int GM, bool BUF = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmProblem p1, int tiles0, int ntm0,
                                                           int ntm1, int total_tiles, int per_xcd) {
   using namespace gk;
@@ -151,6 +161,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
   // ---- two load streams (A and W), each with its own tile / slab cursor
   const bf16 *a_src[LDA];
   const bf16 *b_src[LDB];
+  // BUF: buffer loads; per-lane 32-bit byte offsets, the slab's k offset in
+  // the scalar offset, one resource per operand (two for w1 | w3)
+  int a_off[LDA], b_off[LDB];
+  const void *a_base = nullptr, *b_base = nullptr, *b3_base = nullptr;
+  int a_bytes = 0, b_bytes = 0;
   int at = t_first, akt = 0, apos = 0;
   int bt = t_first, bkt = 0, bpos = 0;
 #define A_SETUP(t_)                                                                                       \
@@ -163,7 +178,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
     _Pragma("unroll") for (int i = 0; i < LDA; ++i) {                                                     \
       const int r = i * ROWS_PER_ROUND + wave * 8 + lrow;                                                 \
       const int gr = m0_ + r < M_ ? m0_ + r : M_ - 1;                                                     \
-      a_src[i] = A_ + (int64_t)gr * K + (lslot ^ swz(r)) * 8;                                             \
+      if constexpr (BUF) a_off[i] = (gr * K + (lslot ^ swz(r)) * 8) * 2;                                  \
+      else a_src[i] = A_ + (int64_t)gr * K + (lslot ^ swz(r)) * 8;                                        \
+    }                                                                                                     \
+    if constexpr (BUF) {                                                                                  \
+      a_base = A_;                                                                                        \
+      a_bytes = M_ * K * 2;                                                                               \
     }                                                                                                     \
   } while (0)
 #define B_SETUP(t_)                                                                                       \
@@ -173,27 +193,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
     tile_coords(t_, tiles0, ntm0, ntm1, ntn, GM, BM, OUTC, sec_, m0_, n0_);                               \
     const bf16 *W_ = (const bf16 *)(sec_ ? p1.W : p0.W);                                                  \
     const bf16 *W3_ = (const bf16 *)(sec_ ? p1.W3 : p0.W3);                                               \
+    const int N_ = p0.N;                                                                                  \
     _Pragma("unroll") for (int i = 0; i < LDB; ++i) {                                                     \
       const int r = i * ROWS_PER_ROUND + wave * 8 + lrow;                                                 \
-      const bf16 *base_;                                                                                  \
-      if constexpr (SWI) {                                                                                \
-        base_ = r < BN / 2 ? W_ + (int64_t)(n0_ + r) * K : W3_ + (int64_t)(n0_ + r - BN / 2) * K;         \
+      if constexpr (BUF) {                                                                                \
+        const int wr_ = SWI && r >= BN / 2 ? r - BN / 2 : r;                                              \
+        b_off[i] = ((n0_ + wr_) * K + (lslot ^ swz(r)) * 8) * 2;                                          \
       } else {                                                                                            \
-        base_ = W_ + (int64_t)(n0_ + r) * K;                                                              \
+        const bf16 *base_;                                                                                \
+        if constexpr (SWI) {                                                                              \
+          base_ = r < BN / 2 ? W_ + (int64_t)(n0_ + r) * K : W3_ + (int64_t)(n0_ + r - BN / 2) * K;       \
+        } else {                                                                                          \
+          base_ = W_ + (int64_t)(n0_ + r) * K;                                                            \
+        }                                                                                                 \
+        b_src[i] = base_ + (lslot ^ swz(r)) * 8;                                                          \
       }                                                                                                   \
-      b_src[i] = base_ + (lslot ^ swz(r)) * 8;                                                            \
+    }                                                                                                     \
+    if constexpr (BUF) {                                                                                  \
+      b_base = W_;                                                                                        \
+      b3_base = W3_;                                                                                      \
+      b_bytes = N_ * K * 2;                                                                               \
     }                                                                                                     \
   } while (0)
 // one load instruction (part i) of the current A / W slab, and the cursor
 // step once all parts of the slab are out
 #define ISSUE_A_PART(i_)                                                                                   \
-  __builtin_amdgcn_global_load_lds((const void *)(a_src[i_] + akt * RBK),                                  \
-                                   (lds_void *)(a_ring + apos * A_UNIT + dst0 + (i_) * ROWS_PER_ROUND * RROW), \
-                                   16, 0, 0)
+  do {                                                                                                     \
+    lds_void *d_ = (lds_void *)(a_ring + apos * A_UNIT + dst0 + (i_) * ROWS_PER_ROUND * RROW);             \
+    if constexpr (BUF)                                                                                     \
+      buffer_lds16(a_base, a_bytes, d_, a_off[i_], akt * RBK * 2);                                         \
+    else                                                                                                   \
+      __builtin_amdgcn_global_load_lds((const void *)(a_src[i_] + akt * RBK), d_, 16, 0, 0);               \
+  } while (0)
 #define ISSUE_B_PART(i_)                                                                                   \
-  __builtin_amdgcn_global_load_lds((const void *)(b_src[i_] + bkt * RBK),                                  \
-                                   (lds_void *)(b_ring + bpos * B_UNIT + dst0 + (i_) * ROWS_PER_ROUND * RROW), \
-                                   16, 0, 0)
+  do {                                                                                                     \
+    lds_void *d_ = (lds_void *)(b_ring + bpos * B_UNIT + dst0 + (i_) * ROWS_PER_ROUND * RROW);             \
+    if constexpr (BUF) {                                                                                   \
+      const void *bb_ = SWI && (i_) * ROWS_PER_ROUND >= BN / 2 ? b3_base : b_base;                        \
+      buffer_lds16(bb_, b_bytes, d_, b_off[i_], bkt * RBK * 2);                                            \
+    } else {                                                                                               \
+      __builtin_amdgcn_global_load_lds((const void *)(b_src[i_] + bkt * RBK), d_, 16, 0, 0);               \
+    }                                                                                                      \
+  } while (0)
 #define STEP_A()                                                                                           \
   do {                                                                                                     \
     apos = apos + 1 == NA ? 0 : apos + 1;                                                                  \
@@ -442,7 +483,7 @@ int cu_count() {
 // Both problems of a grouped launch must share N and K (the image and text
 // weights of one layer do); N must be a multiple of the tile's output
 // columns and K of the slab depth.
-template <int BM, int BN, int WM, int WN, int EPI, int GM = 4>
+template <int BM, int BN, int WM, int WN, int EPI, int GM = 4, bool BUF = false>
 hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st) {
   const int outc = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   if (np > 1 && (pr[0].N != pr[1].N || pr[0].K != pr[1].K)) return hipErrorInvalidValue;
@@ -459,7 +500,7 @@ hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st) {
   if (grid > per_xcd * 8) grid = per_xcd * 8;
   GemmProblem q0 = pr[0], q1 = np > 1 ? pr[1] : pr[0];
   if (tiles[0] == 0) q0 = q1;
-  hipLaunchKernelGGL((gemm_bf16<BM, BN, WM, WN, EPI, GM>), dim3(grid), dim3(64 * WM * WN), 0, st, q0, q1, tiles[0],
+  hipLaunchKernelGGL((gemm_bf16<BM, BN, WM, WN, EPI, GM, BUF>), dim3(grid), dim3(64 * WM * WN), 0, st, q0, q1, tiles[0],
                      ntm[0] > 0 ? ntm[0] : 1, ntm[1] > 0 ? ntm[1] : 1, total, per_xcd);
   return hipGetLastError();
 }
@@ -548,12 +589,18 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st) {
     if (pr[i].N % outc) n256 = false;
     tiles256 += ((pr[i].M + 255) / 256) * (pr[i].N / outc);
   }
+  // buffer loads (32-bit offsets) whenever every operand spans < 2 GiB
+  bool buf = true;
+  for (int i = 0; i < np; ++i)
+    if ((int64_t)pr[i].M * pr[i].K * 2 >= (int64_t(1) << 31) || (int64_t)pr[i].N * pr[i].K * 2 >= (int64_t(1) << 31))
+      buf = false;
   if (!n256) {
     if constexpr (SWI) return hipErrorInvalidValue;
-    else return run_bf16<256, 128, 4, 2, EPI>(pr, np, st);
+    else return buf ? run_bf16<256, 128, 4, 2, EPI, 4, true>(pr, np, st) : run_bf16<256, 128, 4, 2, EPI>(pr, np, st);
   }
-  if (tiles256 * 2 < cu_count()) return run_bf16<128, 256, 2, 4, EPI>(pr, np, st);
-  return run_bf16<256, 256, 2, 4, EPI>(pr, np, st);
+  if (tiles256 * 2 < cu_count())
+    return buf ? run_bf16<128, 256, 2, 4, EPI, 4, true>(pr, np, st) : run_bf16<128, 256, 2, 4, EPI>(pr, np, st);
+  return buf ? run_bf16<256, 256, 2, 4, EPI, 4, true>(pr, np, st) : run_bf16<256, 256, 2, 4, EPI>(pr, np, st);
 }
 
 hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream) {
