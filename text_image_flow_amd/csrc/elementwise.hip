@@ -192,7 +192,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
 
 // ------------------------------------------------ skinny GEMM (GEMV)
 // y[b, n] = sum_k f(x[b, k]) W[n, k] + bias[n] for b < B (B <= 8 per launch).
-// HBM-bound on W, which is read exactly once for all B samples.  Each wave
+// HBM-bound on W, which is read exactly once for all B samples.  (fp32 weights;
+// bf16 weights use gemv_bf16_kernel below.)  Each wave
 // keeps f(x) for its k-range in registers (lane l owns k = 8 l + 512 i) and
 // handles 8 rows at a time with all of their 16-byte weight loads issued
 // before any FMA, so many loads are in flight per lane.
@@ -281,6 +282,103 @@ hipError_t gemv_run(const GemvBatch &g, const float *x, int K, bool silu_in, hip
   return hipGetLastError();
 }
 
+// bf16 weights: the block stages f(x) for all its samples in LDS once (the
+// four waves share it; f is SiLU when silu_in), each wave keeps its k-range
+// of f(x) in registers and walks GEMV_RW rows, 8 at a time, with the 8 rows'
+// 16-byte loads for all KC k-chunks in flight together.  Long-lived waves
+// amortise the staging; KC = ceil(K / 512) sizes the register arrays.
+constexpr int GEMV_RW = 64;       // rows per wave
+
+template <int NB, int KC>
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvBatch g, const float *x, int K, int silu_in) {
+  __shared__ float sx[NB * GEMV_MAXK];
+  for (int i = threadIdx.x; i < NB * K; i += 256) {
+    const float v = x[i];
+    sx[i] = silu_in ? silu_f(v) : v;
+  }
+  __syncthreads();
+  const int prob = blockIdx.y;
+  const int N = g.N[prob];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rowb = (blockIdx.x * GEMV_WAVES + wave) * GEMV_RW;
+  if (rowb >= N) return;
+  float fx[NB][KC][8];
+#pragma unroll
+  for (int c = 0; c < KC; ++c)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = c * 512 + lane * 8 + e;
+        fx[b][c][e] = k < K ? sx[b * K + k] : 0.f;
+      }
+  const bf16 *W = (const bf16 *)g.W[prob];
+  const bf16 *bias = (const bf16 *)g.bias[prob];
+#pragma unroll 1
+  for (int rg = 0; rg < GEMV_RW; rg += GEMV_ROWS) {
+    const int row0 = rowb + rg;
+    if (row0 >= N) break;
+    bf16x8 wv[KC][GEMV_ROWS];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int k = c * 512 + lane * 8;
+#pragma unroll
+      for (int r = 0; r < GEMV_ROWS; ++r) {
+        const int n = row0 + r < N ? row0 + r : N - 1;
+        wv[c][r] = k < K ? *(const bf16x8 *)(W + (int64_t)n * K + k) : bf16x8{};
+      }
+    }
+    float acc[GEMV_ROWS][NB];
+#pragma unroll
+    for (int r = 0; r < GEMV_ROWS; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int r = 0; r < GEMV_ROWS; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][b] = fmaf((float)wv[c][r][e], fx[b][c][e], acc[r][b]);
+#pragma unroll
+    for (int r = 0; r < GEMV_ROWS; ++r) {
+      const int n = row0 + r;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float v = wave_sum(acc[r][b]);
+        if (lane == 0 && n < N) g.y[prob][(int64_t)b * g.y_stride[prob] + n] = v + (bias ? (float)bias[n] : 0.f);
+      }
+    }
+  }
+}
+
+template <int NB, int KC>
+hipError_t gemv_bf16_run(const GemvBatch &g, const float *x, int K, bool silu_in, hipStream_t st) {
+  int maxN = 0;
+  for (int i = 0; i < g.nprob; ++i) maxN = g.N[i] > maxN ? g.N[i] : maxN;
+  const int rows_per_block = GEMV_WAVES * GEMV_RW;
+  dim3 grid((maxN + rows_per_block - 1) / rows_per_block, g.nprob);
+  hipLaunchKernelGGL((gemv_bf16_kernel<NB, KC>), grid, dim3(256), 0, st, g, x, K, silu_in ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int NB>
+hipError_t gemv_bf16_kc(const GemvBatch &g, const float *x, int K, bool silu_in, hipStream_t st) {
+  switch ((K + 511) / 512) {
+    case 1: return gemv_bf16_run<NB, 1>(g, x, K, silu_in, st);
+    case 2: return gemv_bf16_run<NB, 2>(g, x, K, silu_in, st);
+    case 3: return gemv_bf16_run<NB, 3>(g, x, K, silu_in, st);
+    default: return gemv_bf16_run<NB, 4>(g, x, K, silu_in, st);
+  }
+}
+
+template <typename T, int NB>
+hipError_t gemv_pick(const GemvBatch &g, const float *x, int K, bool silu_in, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) return gemv_bf16_kc<NB>(g, x, K, silu_in, st);
+  else return gemv_run<T, NB>(g, x, K, silu_in, st);
+}
+
 template <typename T>
 hipError_t gemv_dispatch(const GemvBatch &g, const float *x, int B, int K, bool silu_in, hipStream_t st) {
   // batches larger than 8 run as several launches on row offsets of x / y
@@ -291,14 +389,14 @@ hipError_t gemv_dispatch(const GemvBatch &g, const float *x, int B, int K, bool 
     const float *xx = x + (int64_t)b0 * K;
     hipError_t e;
     switch (nb) {
-      case 1: e = gemv_run<T, 1>(gg, xx, K, silu_in, st); break;
-      case 2: e = gemv_run<T, 2>(gg, xx, K, silu_in, st); break;
-      case 3: e = gemv_run<T, 3>(gg, xx, K, silu_in, st); break;
-      case 4: e = gemv_run<T, 4>(gg, xx, K, silu_in, st); break;
-      case 5: e = gemv_run<T, 5>(gg, xx, K, silu_in, st); break;
-      case 6: e = gemv_run<T, 6>(gg, xx, K, silu_in, st); break;
-      case 7: e = gemv_run<T, 7>(gg, xx, K, silu_in, st); break;
-      default: e = gemv_run<T, 8>(gg, xx, K, silu_in, st); break;
+      case 1: e = gemv_pick<T, 1>(gg, xx, K, silu_in, st); break;
+      case 2: e = gemv_pick<T, 2>(gg, xx, K, silu_in, st); break;
+      case 3: e = gemv_pick<T, 3>(gg, xx, K, silu_in, st); break;
+      case 4: e = gemv_pick<T, 4>(gg, xx, K, silu_in, st); break;
+      case 5: e = gemv_pick<T, 5>(gg, xx, K, silu_in, st); break;
+      case 6: e = gemv_pick<T, 6>(gg, xx, K, silu_in, st); break;
+      case 7: e = gemv_pick<T, 7>(gg, xx, K, silu_in, st); break;
+      default: e = gemv_pick<T, 8>(gg, xx, K, silu_in, st); break;
     }
     if (e != hipSuccess) return e;
   }
