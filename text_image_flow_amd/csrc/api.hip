@@ -140,7 +140,7 @@ struct BlockWs {
   float *mod;                 // [2][B][6D]
   void *a_img, *a_txt;        // [B*S, D] act: norm output, then attention output
   void *qkv_img, *qkv_txt;    // [B*S, 3D] act; reused for the SwiGLU output [B*S, mlp]
-  void *Q, *K, *Vt;           // joint layout
+  void *Q, *K, *V;            // joint layout [B, H, S_pad, 64]
   size_t bytes;
 };
 
@@ -165,7 +165,7 @@ BlockWs carve_block(const lens_config *c, int B, int Si, int St, char *base, boo
   w.qkv_txt = take((size_t)B * St * wide * es);
   w.Q = take((size_t)B * c->heads * Sp * 64 * es);
   w.K = take((size_t)B * c->heads * Sp * 64 * es);
-  w.Vt = take((size_t)B * c->heads * Sp * 64 * es);
+  w.V = take((size_t)B * c->heads * Sp * 64 * es);
   w.bytes = off;
   return w;
 }
@@ -239,20 +239,19 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   g[0] = GemmProblem{ws.a_img, w->img.qkv.w, nullptr, w->img.qkv.b, nullptr, ws.qkv_img, nullptr, 0, 1, Mi, 3 * D, D};
   g[1] = GemmProblem{ws.a_txt, w->txt.qkv.w, nullptr, w->txt.qkv.b, nullptr, ws.qkv_txt, nullptr, 0, 1, Mt, 3 * D, D};
   LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE, bf, g, 2, st));
-  // 3. QK RMSNorm + RoPE -> joint Q, K, V^T
+  // 3. QK RMSNorm + RoPE -> joint Q, K, V
   const int Sp = s_pad(Si, St);
   QkRopeArgs qa{ws.qkv_img, ws.qkv_txt, w->img.q_gain, w->img.k_gain, w->txt.q_gain, w->txt.k_gain, img_pos, txt_pos,
-                ws.Q, ws.K, ws.Vt, B, c->heads, Si, St, Sp, c->rope_axes[0], c->rope_axes[1], c->rope_axes[2],
+                ws.Q, ws.K, ws.V, B, c->heads, Si, St, Sp, c->rope_axes[0], c->rope_axes[1], c->rope_axes[2],
                 c->rope_theta, c->eps,
-                bf ? 0.125f * 1.4426950408889634f : 1.0f,   // bf16 attention takes Q in log2 units
-                bf ? 1 : 0};
+                bf ? 0.125f * 1.4426950408889634f : 1.0f};  // bf16 attention takes Q in log2 units
   {
     Timed t(LENS_KERNEL_QKNORM_ROPE, st);
     e = t.done(launch_qknorm_rope(qa, bf, st));
     if (e != hipSuccess) return fail(LENS_ERR_HIP, "qk-norm/rope launch failed: %s", hipGetErrorString(e));
   }
   // 4. joint attention; outputs overwrite the (dead) norm outputs
-  AttnArgs aa{ws.Q, ws.K, ws.Vt, ws.a_img, ws.a_txt, txt_len, B, c->heads, Si, St, Sp, 0.125f};
+  AttnArgs aa{ws.Q, ws.K, ws.V, ws.a_img, ws.a_txt, txt_len, B, c->heads, Si, St, Sp, 0.125f};
   {
     Timed t(LENS_KERNEL_ATTENTION, st);
     e = t.done(launch_attention(aa, bf, st));

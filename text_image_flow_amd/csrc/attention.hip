@@ -81,6 +81,39 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
+// V tiles are row-major [key][64 dims] like K tiles, 16-byte chunk c of
+// key row r in slot c ^ vswz(r).  The PV MFMA wants V^T fragments (row =
+// dim, k = keys), which ds_read_tr16_b64 assembles: within each 16-lane
+// group, lane j reads 4 consecutive dims of key j / 4 and lane i gets back
+// dim i of those 4 keys.  The 8 keys a lane feeds per k-step follow the
+// P^T operand's k-slot order (slot s holds key s with bits 2 and 3
+// swapped): keys 4 hl .. 4 hl + 3 and 8 + 4 hl .. 8 + 4 hl + 3.  vswz puts
+// the 4 key rows one 16-lane read touches on 8 distinct bank groups.
+__device__ __forceinline__ int vswz(int r) { return ((r >> 1) & 1) * 4; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// byte offset inside a V tile of lane's first transpose read for k-step 0,
+// dim half 0 (vlane), and the fragment for (ks, dh)
+__device__ __forceinline__ int v_lane_row(int lane) { return 4 * (lane >> 5) + ((lane & 15) >> 2); }
+__device__ __forceinline__ int v_lane_dim(int lane) { return ((lane >> 4) & 1) * 16 + 4 * (lane & 3); }
+__device__ __forceinline__ bf16x8 v_frag(const char *sVb, int ks, int dh, int lane) {
+  const int dim = dh * 32 + v_lane_dim(lane);
+  bf16x8 v;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int key = ks * 16 + 8 * r + v_lane_row(lane);
+    const int off = key * 128 + (((dim >> 3) ^ vswz(key)) << 4) + (dim & 7) * 2;
+    const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)((__attribute__((address_space(3))) char *)sVb + off));
+    const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * r + e] = tb[e];
+  }
+  return v;
+}
+
 // One 64-key tile.  FIRST: the S accumulators start at 0, the tile's max
 // becomes the running max m and p = exp2(s - m).  Otherwise they start at
 // minit = -m (16 copies), so the MFMAs deliver s - m directly and p = exp2(.)
@@ -91,6 +124,7 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
                                              float &m_run, float &l_run, f32x16 &minit, int kv0, int n_kv, int ql,
                                              int hl) {
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  const int vlane = hl * 32 + ql;
   const int sw = (ql >> 1) & 7;   // rows ql and 32 + ql share the swizzle
   f32x16 s0, s1;
   {
@@ -166,9 +200,8 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
   l_run += lsum;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int slot = ((ks * 2 + hl) ^ sw) << 4;
-    const bf16x8 v0 = *(const bf16x8 *)(sVb + ql * 128 + slot);
-    const bf16x8 v1 = *(const bf16x8 *)(sVb + (32 + ql) * 128 + slot);
+    const bf16x8 v0 = v_frag(sVb, ks, 0, vlane);
+    const bf16x8 v1 = v_frag(sVb, ks, 1, vlane);
     o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb[ks], o[0], 0, 0, 0);
     o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb[ks], o[1], 0, 0, 0);
   }
@@ -187,7 +220,7 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   const int64_t bh = (int64_t)b * a.H + h;
   const bf16 *Qg = (const bf16 *)a.Q + bh * a.S_pad * 64;
   const bf16 *Kg = (const bf16 *)a.K + bh * a.S_pad * 64;
-  const bf16 *Vg = (const bf16 *)a.Vt + bh * 64 * a.S_pad;
+  const bf16 *Vg = (const bf16 *)a.V + bh * a.S_pad * 64;
   const int n_kv = kv_count(a, b);
   const int n_tiles = (n_kv + KV_T - 1) / KV_T;
   const int n_full = n_kv / KV_T;
@@ -201,18 +234,18 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const bf16x8 *)(src + ks * 16);
   }
-  // each wave fills rows [wave * 16, wave * 16 + 16) of the K and V^T tiles:
+  // each wave fills rows [wave * 16, wave * 16 + 16) of the K and V tiles:
   // two instructions of 8 rows each; lane -> row + lane / 8, slot lane % 8
   const int r0 = wave * 16 + (lane >> 3), r1 = r0 + 8, slot = lane & 7;
   const bf16 *k_src0 = Kg + (int64_t)r0 * 64 + ((slot ^ ((r0 >> 1) & 7)) * 8);
   const bf16 *k_src1 = Kg + (int64_t)r1 * 64 + ((slot ^ ((r1 >> 1) & 7)) * 8);
-  const bf16 *v_src0 = Vg + (int64_t)r0 * a.S_pad + ((slot ^ ((r0 >> 1) & 7)) * 8);
-  const bf16 *v_src1 = Vg + (int64_t)r1 * a.S_pad + ((slot ^ ((r1 >> 1) & 7)) * 8);
+  const bf16 *v_src0 = Vg + (int64_t)r0 * 64 + ((slot ^ vswz(r0)) * 8);
+  const bf16 *v_src1 = Vg + (int64_t)r1 * 64 + ((slot ^ vswz(r1)) * 8);
   const int dst0 = wave * 16 * 128, dst1 = dst0 + 8 * 128;
 #define ATT_ISSUE(t_)                                                                                       \
   do {                                                                                                      \
     char *sb_ = smem + ((t_) & 1) * STAGE;                                                                  \
-    const int64_t ko_ = (int64_t)(t_) * KV_T * 64, vo_ = (int64_t)(t_) * KV_T;                            \
+    const int64_t ko_ = (int64_t)(t_) * KV_T * 64, vo_ = ko_;                                              \
     __builtin_amdgcn_global_load_lds((const void *)(k_src0 + ko_), (lds_void_t *)(sb_ + dst0), 16, 0, 0);  \
     __builtin_amdgcn_global_load_lds((const void *)(k_src1 + ko_), (lds_void_t *)(sb_ + dst1), 16, 0, 0);  \
     __builtin_amdgcn_global_load_lds((const void *)(v_src0 + vo_), (lds_void_t *)(sb_ + TILE_BYTES + dst0), \
@@ -278,7 +311,7 @@ __global__ __launch_bounds__(64) void attn_f32_simple(AttnArgs a) {
   const int64_t bh = (int64_t)b * a.H + h;
   const float *Qg = (const float *)a.Q + bh * a.S_pad * 64;
   const float *Kg = (const float *)a.K + bh * a.S_pad * 64;
-  const float *Vg = (const float *)a.Vt + bh * 64 * a.S_pad;
+  const float *Vg = (const float *)a.V + bh * a.S_pad * 64;
   const int n_kv = kv_count(a, b);
   float q[64], o[64];
   const int pr = p < S ? p : S - 1;
@@ -292,7 +325,7 @@ __global__ __launch_bounds__(64) void attn_f32_simple(AttnArgs a) {
     for (int e = threadIdx.x; e < 64 * 64; e += 64) {
       const int r = e / 64, d = e % 64;
       sK[r][d] = Kg[(int64_t)(kv0 + r) * 64 + d];
-      sV[r][d] = Vg[(int64_t)r * a.S_pad + kv0 + d];
+      sV[d][r] = Vg[(int64_t)(kv0 + r) * 64 + d];
     }
     __syncthreads();
     const int nk = n_kv - kv0 < 64 ? n_kv - kv0 : 64;

@@ -50,14 +50,14 @@ struct GemmProblem {
 // Grouped launch of up to 2 problems that share N, K and the epilogue.
 hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream);
 
-// Joint attention.  Q, K: [B, H, S_pad, 64]; Vt: [B, H, 64, S_pad] (act type).
-// bf16 path: Q pre-scaled by scale * log2(e), V^T key-permuted (QkRopeArgs);
-// fp32 path: plain Q and V^T, scale applied inside.
+// Joint attention.  Q, K, V: [B, H, S_pad, 64] (act type), rows >= S zero.
+// bf16 path: Q pre-scaled by scale * log2(e) (QkRopeArgs);
+// fp32 path: plain Q, scale applied inside.
 // Output rows p < S_img go to O_img[(b*S_img + p), h*64 + d], rows
 // S_img <= p < S_img + S_txt to O_txt[(b*S_txt + p - S_img), ...].
 // Valid keys of sample b: [0, S_img + clamp(txt_len[b], 0, S_txt)).
 struct AttnArgs {
-  const void *Q, *K, *Vt;
+  const void *Q, *K, *V;
   void *O_img, *O_txt;
   const int32_t *txt_len;  // device, [B] or NULL
   int32_t B, H, S_img, S_txt, S_pad;
@@ -79,18 +79,17 @@ hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float
 
 // QK RMSNorm + RoPE + joint layout.  qkv_img [B*S_img, 3D], qkv_txt [B*S_txt, 3D].
 // q_scale multiplies q after RoPE (the bf16 attention kernel takes Q in
-// log2 units: scale * log2(e)); v_perm != 0 stores V^T with bits 2 and 3 of
-// the key index swapped inside every 16 keys (the bf16 attention layout).
+// log2 units: scale * log2(e)).  Q, K, V out: [B, H, S_pad, 64], rows >= S
+// zero.
 struct QkRopeArgs {
   const void *qkv_img, *qkv_txt;
   const void *qg_img, *kg_img, *qg_txt, *kg_txt;  // [64] act type
   const int32_t *pos_img, *pos_txt;               // [S, 3]
-  void *Q, *K, *Vt;
+  void *Q, *K, *V;
   int32_t B, H, S_img, S_txt, S_pad;
   int32_t axes0, axes1, axes2;
   float theta, eps;
   float q_scale;
-  int32_t v_perm;
 };
 hipError_t launch_qknorm_rope(const QkRopeArgs &a, bool bf16_path, hipStream_t stream);
 

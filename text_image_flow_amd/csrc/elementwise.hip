@@ -104,7 +104,6 @@ __device__ __forceinline__ void store16<bf16>(bf16 *dst, const float *v) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
-  __shared__ float sV[64][64 + 1];
   const int b = blockIdx.z, h = blockIdx.y;
   const int t = threadIdx.x, tok = t >> 2, qd = t & 3, d0 = qd * 16;
   const int p = blockIdx.x * 64 + tok;
@@ -175,19 +174,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
   }
   store16<T>(Qo, q);
   store16<T>(Ko, k);
-  for (int i = 0; i < 16; ++i) sV[d0 + i][tok] = v[i];
-  __syncthreads();
-  // V^T [d][p]: thread t writes d = t/4, positions (t%4)*16 .. +16; with
-  // v_perm, position j of the 16 holds key j with bits 2 and 3 swapped
-  {
-    const int d = t >> 2, c0 = (t & 3) * 16;
-    float tmp[16];
-    for (int i = 0; i < 16; ++i) {
-      const int src = a.v_perm ? ((i & 3) | ((i & 4) << 1) | ((i & 8) >> 1)) : i;
-      tmp[i] = sV[d][c0 + src];
-    }
-    store16<T>((T *)a.Vt + (bh * 64 + d) * a.S_pad + blockIdx.x * 64 + c0, tmp);
-  }
+  store16<T>((T *)a.V + (bh * a.S_pad + p) * 64 + d0, v);
 }
 
 // ------------------------------------------------ skinny GEMM (GEMV)

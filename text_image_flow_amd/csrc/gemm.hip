@@ -484,7 +484,7 @@ int cu_count() {
 // weights of one layer do); N must be a multiple of the tile's output
 // columns and K of the slab depth.
 template <int BM, int BN, int WM, int WN, int EPI, int GM = 4, bool BUF = false>
-hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st) {
+hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st, int max_grid = 0) {
   const int outc = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   if (np > 1 && (pr[0].N != pr[1].N || pr[0].K != pr[1].K)) return hipErrorInvalidValue;
   if (pr[0].N % outc || pr[0].K % gk::RBK || pr[0].K <= 0) return hipErrorInvalidValue;
@@ -496,7 +496,7 @@ hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st) {
   const int total = tiles[0] + tiles[1];
   if (total == 0) return hipSuccess;
   const int per_xcd = (total + 7) / 8;
-  int grid = cu_count() / 8 * 8;
+  int grid = (max_grid > 0 ? max_grid : cu_count()) / 8 * 8;
   if (grid > per_xcd * 8) grid = per_xcd * 8;
   GemmProblem q0 = pr[0], q1 = np > 1 ? pr[1] : pr[0];
   if (tiles[0] == 0) q0 = q1;
