@@ -141,6 +141,7 @@ struct BlockWs {
   void *a_img, *a_txt;        // [B*S, D] act: norm output, then attention output
   void *qkv_img, *qkv_txt;    // [B*S, 3D] act; reused for the SwiGLU output [B*S, mlp]
   void *Q, *K, *V;            // joint layout [B, H, S_pad, 64]
+  float2 *rope;               // bf16 path: [S_img + S_txt][32] (cos, sin)
   size_t bytes;
 };
 
@@ -166,6 +167,7 @@ BlockWs carve_block(const lens_config *c, int B, int Si, int St, char *base, boo
   w.Q = take((size_t)B * c->heads * Sp * 64 * es);
   w.K = take((size_t)B * c->heads * Sp * 64 * es);
   w.V = take((size_t)B * c->heads * Sp * 64 * es);
+  w.rope = (float2 *)take((size_t)(Si + St) * 32 * sizeof(float2));
   w.bytes = off;
   return w;
 }
@@ -216,6 +218,21 @@ lens_status gemm(lens_kernel_kind, int epi, bool bf, GemmProblem *p, int np, hip
     if (_s != LENS_OK) return _s;    \
   } while (0)
 
+// bf16 path, once per forward call: the RoPE table of the joint sequence
+// (shared by every block) and zeroed padding rows of Q, K, V (the QKV
+// epilogue writes valid rows only; V rows beyond the last key must be finite).
+lens_status prepare_joint(const lens_config *c, const int32_t *img_pos, const int32_t *txt_pos, int B, int Si, int St,
+                          const BlockWs &ws, hipStream_t st) {
+  if (c->act_dtype != LENS_BF16) return LENS_OK;
+  Timed t(LENS_KERNEL_QKNORM_ROPE, st);
+  hipError_t e = launch_rope_table(img_pos, txt_pos, Si, St, c->rope_axes[0], c->rope_axes[1], c->rope_axes[2],
+                                   c->rope_theta, ws.rope, st);
+  if (e == hipSuccess) e = launch_zero_pad_rows(ws.Q, ws.K, ws.V, B, c->heads, Si + St, s_pad(Si, St), st);
+  e = t.done(e);
+  if (e != hipSuccess) return fail(LENS_ERR_HIP, "RoPE table / padding launch failed: %s", hipGetErrorString(e));
+  return LENS_OK;
+}
+
 // The block after AdaLN: mod_img / mod_txt point at [B][6D] rows.
 lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img, float *h_txt, const float *mod_img,
                        const float *mod_txt, const int32_t *img_pos, const int32_t *txt_pos, const int32_t *txt_len,
@@ -234,20 +251,27 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
     e = t.done(launch_norm_modulate(nm, 2, D, c->eps, bf, st));
     if (e != hipSuccess) return fail(LENS_ERR_HIP, "norm launch failed: %s", hipGetErrorString(e));
   }
-  // 2. QKV projections
+  // 2. QKV projections, 3. QK RMSNorm + RoPE -> joint Q, K, V.  bf16: one
+  // GEMM whose epilogue normalises, rotates and scatters the heads (the
+  // RoPE table and zeroed padding rows come from prepare_joint); fp32:
+  // GEMM into qkv, then the separate QK-norm/RoPE kernel.
   GemmProblem g[2] = {};
   g[0] = GemmProblem{ws.a_img, w->img.qkv.w, nullptr, w->img.qkv.b, nullptr, ws.qkv_img, nullptr, 0, 1, Mi, 3 * D, D};
   g[1] = GemmProblem{ws.a_txt, w->txt.qkv.w, nullptr, w->txt.qkv.b, nullptr, ws.qkv_txt, nullptr, 0, 1, Mt, 3 * D, D};
-  LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE, bf, g, 2, st));
-  // 3. QK RMSNorm + RoPE -> joint Q, K, V
   const int Sp = s_pad(Si, St);
-  QkRopeArgs qa{ws.qkv_img, ws.qkv_txt, w->img.q_gain, w->img.k_gain, w->txt.q_gain, w->txt.k_gain, img_pos, txt_pos,
-                ws.Q, ws.K, ws.V, B, c->heads, Si, St, Sp, c->rope_axes[0], c->rope_axes[1], c->rope_axes[2],
-                c->rope_theta, c->eps,
-                bf ? 0.125f * 1.4426950408889634f : 1.0f};  // bf16 attention takes Q in log2 units
-  {
+  if (bf) {
+    QkvOut qo{ws.Q, ws.K, ws.V, {w->img.q_gain, w->txt.q_gain}, {w->img.k_gain, w->txt.k_gain}, ws.rope,
+              Si, St, Sp, c->heads, c->eps, 0.125f * 1.4426950408889634f};   // attention takes Q in log2 units
+    Timed t(LENS_KERNEL_GEMM, st);
+    e = t.done(launch_gemm(EPI_QKV, true, g, 2, st, &qo));
+    if (e != hipSuccess) return fail(LENS_ERR_HIP, "QKV GEMM launch failed: %s", hipGetErrorString(e));
+  } else {
+    LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE, bf, g, 2, st));
+    QkRopeArgs qa{ws.qkv_img, ws.qkv_txt, w->img.q_gain, w->img.k_gain, w->txt.q_gain, w->txt.k_gain, img_pos,
+                  txt_pos, ws.Q, ws.K, ws.V, B, c->heads, Si, St, Sp, c->rope_axes[0], c->rope_axes[1],
+                  c->rope_axes[2], c->rope_theta, c->eps, 1.0f};
     Timed t(LENS_KERNEL_QKNORM_ROPE, st);
-    e = t.done(launch_qknorm_rope(qa, bf, st));
+    e = t.done(launch_qknorm_rope(qa, false, st));
     if (e != hipSuccess) return fail(LENS_ERR_HIP, "qk-norm/rope launch failed: %s", hipGetErrorString(e));
   }
   // 4. joint attention; outputs overwrite the (dead) norm outputs
@@ -370,6 +394,7 @@ lens_status lens_block_forward(const lens_config *c, const lens_block_w *w, floa
   const lens_block_w *bl[1] = {w};
   LTRY(adaln_all(c, bl, 1, temb, B, ws.mod, st));
   const float *mod_img = ws.mod, *mod_txt = ws.mod + (size_t)B * 6 * c->hidden;
+  LTRY(prepare_joint(c, img_pos, txt_pos, B, Si, St, ws, st));
   return block_core(c, w, h_img, h_txt, mod_img, mod_txt, img_pos, txt_pos, txt_len, B, Si, St, ws, st);
 }
 
@@ -449,6 +474,7 @@ lens_status lens_dit_forward(const lens_config *c, const lens_dit_w *w, const vo
     LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE_F32, bf, &g, 1, st));
   }
   // blocks
+  LTRY(prepare_joint(c, img_pos, txt_pos, B, Si, St, ws.blk, st));
   for (int i = 0; i < c->n_blocks; ++i) {
     const float *mi = ws.mods + (size_t)i * 2 * B * 6 * D;
     const float *mt = mi + (size_t)B * 6 * D;

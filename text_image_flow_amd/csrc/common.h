@@ -30,7 +30,10 @@ enum Epilogue {
   EPI_STORE = 0,     // C = acc + bias                    (C in act type)
   EPI_STORE_F32 = 1, // C = acc + bias                    (C float)
   EPI_GATED = 2,     // H += gate[m / rows_per_gate] * (acc + bias)   (H float)
-  EPI_SWIGLU = 3     // C = silu(acc1 + b1) * (acc3 + b3), B rows from w1 and w3
+  EPI_SWIGLU = 3,    // C = silu(acc1 + b1) * (acc3 + b3), B rows from w1 and w3
+  EPI_QKV = 4        // y = acc + bias split into per-head q | k | v (QkvOut; bf16 only):
+                     // q, k RMS-normed with gain and rotated (RoPE), q scaled,
+                     // all three written to the joint [B, H, S_pad, 64] layout
 };
 
 // One GEMM problem: C[M, N] = A[M, K] . W[N, K]^T (+ epilogue).
@@ -47,8 +50,31 @@ struct GemmProblem {
   int32_t M, N, K;
 };
 
-// Grouped launch of up to 2 problems that share N, K and the epilogue.
-hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream);
+// Outputs of the QKV epilogue.  Problem 0 holds the image rows of the batch
+// (b * S_img + p -> joint position p), problem 1 the text rows (b * S_txt + p
+// -> joint position S_img + p).  rope: [S_img + S_txt][32] (cos, sin) of
+// every joint position and rotation pair.
+struct QkvOut {
+  void *Q, *K, *V;                      // [B, H, S_pad, 64] bf16
+  const void *q_gain[2], *k_gain[2];    // per problem, [64] bf16
+  const float2 *rope;
+  int32_t S_img, S_txt, S_pad, H;
+  float eps, q_scale;
+};
+
+// Grouped launch of up to 2 problems that share N, K and the epilogue
+// (qo: EPI_QKV only).
+hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream,
+                       const QkvOut *qo = nullptr);
+
+// RoPE table of the joint sequence: rope[j][i] = (cos, sin) of pos(j)[axis] *
+// theta^(-2 i' / axis_dim) for rotation pair i (pairs 0 .. axes0/2 - 1 on axis
+// 0, then axis 1, then axis 2; i' = index inside the axis), the angles
+// computed exactly as the QK-norm/RoPE kernel does.
+hipError_t launch_rope_table(const int32_t *pos_img, const int32_t *pos_txt, int S_img, int S_txt, int axes0,
+                             int axes1, int axes2, float theta, float2 *rope, hipStream_t stream);
+// Zero rows S .. S_pad - 1 of every (b, h) of the joint Q, K, V (bf16).
+hipError_t launch_zero_pad_rows(void *Q, void *K, void *V, int B, int H, int S, int S_pad, hipStream_t stream);
 
 // Joint attention.  Q, K, V: [B, H, S_pad, 64] (act type), rows >= S zero.
 // bf16 path: Q pre-scaled by scale * log2(e) (QkRopeArgs);

@@ -462,6 +462,63 @@ hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float
   return hipGetLastError();
 }
 
+namespace {
+
+// (cos, sin) of every joint position and rotation pair, with the same
+// angle arithmetic as qknorm_rope_kernel.
+__global__ void rope_table_kernel(const int32_t *pos_img, const int32_t *pos_txt, int S_img, int S_txt, int axes0,
+                                  int axes1, int axes2, float theta, float2 *rope) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (S_img + S_txt) * 32) return;
+  const int jp = idx >> 5, i = idx & 31, d = 2 * i;
+  const int32_t *pos = jp < S_img ? pos_img + 3 * jp : pos_txt + 3 * (jp - S_img);
+  float pa, j, w;
+  if (d < axes0) {
+    pa = (float)pos[0]; j = (float)(d / 2); w = (float)axes0;
+  } else if (d < axes0 + axes1) {
+    pa = (float)pos[1]; j = (float)((d - axes0) / 2); w = (float)axes1;
+  } else {
+    pa = (float)pos[2]; j = (float)((d - axes0 - axes1) / 2); w = (float)axes2;
+  }
+  const float l2t = log2f(theta);
+  const float ang = pa * exp2f(-2.f * j / w * l2t);
+  float sn, cs;
+  sincosf(ang, &sn, &cs);
+  rope[idx] = make_float2(cs, sn);
+}
+
+// one thread per 8 bf16 of a padding row of Q, K and V
+__global__ void zero_pad_kernel(bf16 *Q, bf16 *K, bf16 *V, int S, int S_pad, int64_t n8) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const int npad = S_pad - S;
+  const int64_t bh = i / ((int64_t)npad * 8), rem = i % ((int64_t)npad * 8);
+  const int64_t off = (bh * S_pad + S + rem / 8) * 64 + (rem % 8) * 8;
+  const bf16x8 z = {};
+  *(bf16x8 *)(Q + off) = z;
+  *(bf16x8 *)(K + off) = z;
+  *(bf16x8 *)(V + off) = z;
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(const int32_t *pos_img, const int32_t *pos_txt, int S_img, int S_txt, int axes0,
+                             int axes1, int axes2, float theta, float2 *rope, hipStream_t stream) {
+  const int n = (S_img + S_txt) * 32;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, pos_img, pos_txt, S_img, S_txt,
+                     axes0, axes1, axes2, theta, rope);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_pad_rows(void *Q, void *K, void *V, int B, int H, int S, int S_pad, hipStream_t stream) {
+  const int64_t n8 = (int64_t)B * H * (S_pad - S) * 8;
+  if (n8 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_pad_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, (bf16 *)Q, (bf16 *)K,
+                     (bf16 *)V, S, S_pad, n8);
+  return hipGetLastError();
+}
+
 hipError_t launch_qknorm_rope(const QkRopeArgs &a, bool bf16_path, hipStream_t stream) {
   dim3 grid(a.S_pad / 64, a.H, a.B);
   if (bf16_path)

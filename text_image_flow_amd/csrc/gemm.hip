@@ -120,7 +120,7 @@ __device__ __forceinline__ u32x4 pair_runs(unsigned x0, unsigned x1, unsigned y0
 
 template <int BM, int BN, int WM, int WN, int EPI, int GM, bool BUF = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmProblem p1, int tiles0, int ntm0,
-                                                          int ntm1, int total_tiles, int per_xcd) {
+                                                          int ntm1, int total_tiles, int per_xcd, QkvOut qo) {
   using namespace gk;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -129,6 +129,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
   constexpr int OUTC = SWI ? BN / 2 : BN;
   constexpr int H = SWI ? NT / 2 : NT;          // output sub-tiles per wave along n
   static_assert(!SWI || NT % 2 == 0, "SwiGLU needs an even number of n tiles per wave");
+  static_assert(EPI != EPI_QKV || WTN == 64, "QKV epilogue: one head (64 features) per wave");
   constexpr int NA = 3, NB = 2;                 // ring depths: A two slabs ahead, W one
   constexpr int A_UNIT = BM * RROW, B_UNIT = BN * RROW;
   constexpr int ROWS_PER_ROUND = 8 * NW;        // one wave instruction: 8 rows x 128 B
@@ -383,6 +384,88 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
     out_[2] = bf_lo(hi_);                                                            \
     out_[3] = bf_hi(hi_);                                                            \
   } while (0)
+    if constexpr (EPI == EPI_QKV) {
+      // This wave's 64 features are one head of q, k or v.  Lanes l and
+      // l ^ 32 hold the two halves of a token's head: features
+      // j*32 + 8q + 4*hl + e.
+      const int D = qo.H * 64;
+      const int sect = fw / D, hh = (fw - sect * D) >> 6;
+      bf16 *const dst = (bf16 *)(sect == 0 ? qo.Q : sect == 1 ? qo.K : qo.V);
+      const void *gain = sect == 0 ? qo.q_gain[sec ? 1 : 0] : qo.k_gain[sec ? 1 : 0];
+      const int rps = sec ? qo.S_txt : qo.S_img, joff = sec ? qo.S_img : 0;
+      const float osc = sect == 0 ? qo.q_scale : 1.0f;
+      unsigned bw[2][16], gw[2][16];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        LOAD_BIAS16(bias, j, bw[j]);
+        if (sect < 2) {
+          const cptr gp_ = (cptr)((const bf16 *)gain + j * 32);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) gw[j][k] = gp_[k];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int m = m0 + wm * WTM + i * 32 + frow;
+        const bool ok = m < M;
+        const int mc = ok ? m : 0;
+        const int bsmp = mc / rps, joint = joff + (mc - bsmp * rps);
+        float y[2][4][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float b[4];
+            BIAS4(bw[j], j, q, b);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[j][q][e] = acc[i][j][4 * q + e] + b[e];
+          }
+        if (sect < 2) {
+          // RMSNorm over the head (the partner lane holds the other half)
+          float ss = 0.f;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ss = fmaf(y[j][q][e], y[j][q][e], ss);
+          const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+          const float r = rsqrtf((__uint_as_float(sw_[0]) + __uint_as_float(sw_[1])) / 64.f + qo.eps);
+          const float4 *rope = (const float4 *)(qo.rope + (int64_t)joint * 32);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float g[4];
+              BIAS4(gw[j], j, q, g);
+              // rotation pairs (j*32 + 8q + 4hl)/2 and the next one
+              const float4 cs = rope[(j * 16 + 4 * q + 2 * hl) >> 1];
+#pragma unroll
+              for (int e = 0; e < 4; e += 2) {
+                const float c = e ? cs.z : cs.x, sn = e ? cs.w : cs.y;
+                const float a0 = y[j][q][e] * r * g[e], a1 = y[j][q][e + 1] * r * g[e + 1];
+                y[j][q][e] = (a0 * c - a1 * sn) * osc;
+                y[j][q][e + 1] = (a0 * sn + a1 * c) * osc;
+              }
+            }
+        }
+        bf16 *row = dst + (((int64_t)bsmp * qo.H + hh) * qo.S_pad + joint) * 64;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          unsigned pk[4][2];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            pk[q][0] = pack_bf2(y[j][q][0], y[j][q][1]);
+            pk[q][1] = pack_bf2(y[j][q][2], y[j][q][3]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; q += 2) {
+            const u32x4 o = pair_runs(pk[q][0], pk[q][1], pk[q + 1][0], pk[q + 1][1]);
+            if (ok) *(u32x4 *)(row + j * 32 + 8 * q + 8 * hl) = o;
+          }
+        }
+      }
+    } else {
     const float *gate_row = nullptr;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -453,6 +536,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
         }
       }
     }
+    }
 #undef BIAS4
 #undef LOAD_BIAS16
   }
@@ -484,7 +568,7 @@ int cu_count() {
 // weights of one layer do); N must be a multiple of the tile's output
 // columns and K of the slab depth.
 template <int BM, int BN, int WM, int WN, int EPI, int GM = 4, bool BUF = false>
-hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st, int max_grid = 0) {
+hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st, const QkvOut *qo = nullptr, int max_grid = 0) {
   const int outc = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   if (np > 1 && (pr[0].N != pr[1].N || pr[0].K != pr[1].K)) return hipErrorInvalidValue;
   if (pr[0].N % outc || pr[0].K % gk::RBK || pr[0].K <= 0) return hipErrorInvalidValue;
@@ -500,8 +584,13 @@ hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st, int max_grid 
   if (grid > per_xcd * 8) grid = per_xcd * 8;
   GemmProblem q0 = pr[0], q1 = np > 1 ? pr[1] : pr[0];
   if (tiles[0] == 0) q0 = q1;
+  QkvOut qv = {};
+  if constexpr (EPI == EPI_QKV) {
+    if (!qo) return hipErrorInvalidValue;
+    qv = *qo;
+  }
   hipLaunchKernelGGL((gemm_bf16<BM, BN, WM, WN, EPI, GM, BUF>), dim3(grid), dim3(64 * WM * WN), 0, st, q0, q1, tiles[0],
-                     ntm[0] > 0 ? ntm[0] : 1, ntm[1] > 0 ? ntm[1] : 1, total, per_xcd);
+                     ntm[0] > 0 ? ntm[0] : 1, ntm[1] > 0 ? ntm[1] : 1, total, per_xcd, qv);
   return hipGetLastError();
 }
 
@@ -580,7 +669,7 @@ hipError_t run_f32(const GemmProblem *pr, int np, hipStream_t st) {
 // most CUs idle, or 256 x 128 when N is not a multiple of 256 (N = 128
 // for the final projection).
 template <int EPI>
-hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st) {
+hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st, const QkvOut *qo) {
   constexpr bool SWI = EPI == EPI_SWIGLU;
   const int outc = SWI ? 128 : 256;   // output columns of a 256-wide tile
   bool n256 = true;
@@ -595,21 +684,23 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st) {
     if ((int64_t)pr[i].M * pr[i].K * 2 >= (int64_t(1) << 31) || (int64_t)pr[i].N * pr[i].K * 2 >= (int64_t(1) << 31))
       buf = false;
   if (!n256) {
-    if constexpr (SWI) return hipErrorInvalidValue;
-    else return buf ? run_bf16<256, 128, 4, 2, EPI, 4, true>(pr, np, st) : run_bf16<256, 128, 4, 2, EPI>(pr, np, st);
+    if constexpr (SWI || EPI == EPI_QKV) return hipErrorInvalidValue;
+    else return buf ? run_bf16<256, 128, 4, 2, EPI, 4, true>(pr, np, st, qo) : run_bf16<256, 128, 4, 2, EPI>(pr, np, st, qo);
   }
   if (tiles256 * 2 < cu_count())
-    return buf ? run_bf16<128, 256, 2, 4, EPI, 4, true>(pr, np, st) : run_bf16<128, 256, 2, 4, EPI>(pr, np, st);
-  return buf ? run_bf16<256, 256, 2, 4, EPI, 4, true>(pr, np, st) : run_bf16<256, 256, 2, 4, EPI>(pr, np, st);
+    return buf ? run_bf16<128, 256, 2, 4, EPI, 4, true>(pr, np, st, qo) : run_bf16<128, 256, 2, 4, EPI>(pr, np, st, qo);
+  return buf ? run_bf16<256, 256, 2, 4, EPI, 4, true>(pr, np, st, qo) : run_bf16<256, 256, 2, 4, EPI>(pr, np, st, qo);
 }
 
-hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream) {
+hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream,
+                       const QkvOut *qo) {
   if (bf16_path) {
     switch (epi) {
-      case EPI_STORE: return dispatch_bf16<EPI_STORE>(probs, nprob, stream);
-      case EPI_STORE_F32: return dispatch_bf16<EPI_STORE_F32>(probs, nprob, stream);
-      case EPI_GATED: return dispatch_bf16<EPI_GATED>(probs, nprob, stream);
-      case EPI_SWIGLU: return dispatch_bf16<EPI_SWIGLU>(probs, nprob, stream);
+      case EPI_STORE: return dispatch_bf16<EPI_STORE>(probs, nprob, stream, nullptr);
+      case EPI_STORE_F32: return dispatch_bf16<EPI_STORE_F32>(probs, nprob, stream, nullptr);
+      case EPI_GATED: return dispatch_bf16<EPI_GATED>(probs, nprob, stream, nullptr);
+      case EPI_SWIGLU: return dispatch_bf16<EPI_SWIGLU>(probs, nprob, stream, nullptr);
+      case EPI_QKV: return dispatch_bf16<EPI_QKV>(probs, nprob, stream, qo);
     }
   } else {
     switch (epi) {
