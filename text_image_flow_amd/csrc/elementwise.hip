@@ -34,38 +34,63 @@ __device__ __forceinline__ void store4<bf16>(bf16 *dst, float a, float b, float 
 }
 
 // ------------------------------------------------ RMSNorm + modulation
-// One wave per row; D % 256 == 0 so each lane owns D/256 float4 groups.
+// NORM_RW rows per wave; D % 256 == 0 so each lane owns D/256 float4 groups of a row.
+constexpr int NORM_RW = 2;   // rows per wave of the norm kernel
+
 template <typename T, int G>
-__global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, NormModProblem p1, float eps) {
+__global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, NormModProblem p1, int split0,
+                                                            float eps) {
   constexpr int D = G * 256;
-  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // NORM_RW consecutive rows per wave (problem 0's row count is padded to
+  // split0 so that no wave straddles the two problems); the sample's shift
+  // and scale stay in registers, and the next row's loads go out before this
+  // row's reduction.
+  int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * NORM_RW;
   const int lane = threadIdx.x & 63;
-  const bool second = row >= p0.rows;
+  const bool second = row >= split0;
   const NormModProblem p = second ? p1 : p0;
-  if (second) {
-    row -= p0.rows;
-    if (row >= p1.rows) return;
-  }
-  const float *x = p.h + (int64_t)row * D;
-  const int b = row / p.rows_per_sample;
-  const float *sh = p.shift + (int64_t)b * p.mod_stride;
-  const float *sc = p.scale + (int64_t)b * p.mod_stride;
-  float4 v[G];
-  float ss = 0.f;
+  if (second) row -= split0;
+  const int rows = p.rows;
+  if (row >= rows) return;
+  int cur_b = -1;
+  float4 s4[G], h4[G], v[G];
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    v[i] = *(const float4 *)(x + (i * 64 + lane) * 4);
-    ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
-  }
-  ss = wave_sum(ss);
-  const float r = rsqrtf(ss / (float)D + eps);
-  T *out = (T *)p.out + (int64_t)row * D;
+  for (int i = 0; i < G; ++i) v[i] = *(const float4 *)(p.h + (int64_t)row * D + (i * 64 + lane) * 4);
+  for (int rr = 0; rr < NORM_RW; ++rr) {
+    const int r = row + rr;
+    if (r >= rows) break;
+    const bool more = rr + 1 < NORM_RW && r + 1 < rows;
+    float4 nv[G];
+    if (more) {
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    const int c = (i * 64 + lane) * 4;
-    const float4 s4 = *(const float4 *)(sc + c), h4 = *(const float4 *)(sh + c);
-    store4<T>(out + c, v[i].x * r * (1.f + s4.x) + h4.x, v[i].y * r * (1.f + s4.y) + h4.y,
-              v[i].z * r * (1.f + s4.z) + h4.z, v[i].w * r * (1.f + s4.w) + h4.w);
+      for (int i = 0; i < G; ++i) nv[i] = *(const float4 *)(p.h + (int64_t)(r + 1) * D + (i * 64 + lane) * 4);
+    }
+    const int b = r / p.rows_per_sample;
+    if (b != cur_b) {
+      cur_b = b;
+      const float *sh = p.shift + (int64_t)b * p.mod_stride, *sc = p.scale + (int64_t)b * p.mod_stride;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        s4[i] = *(const float4 *)(sc + (i * 64 + lane) * 4);
+        h4[i] = *(const float4 *)(sh + (i * 64 + lane) * 4);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    ss = wave_sum(ss);
+    const float rs = rsqrtf(ss / (float)D + eps);
+    T *out = (T *)p.out + (int64_t)r * D;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int c = (i * 64 + lane) * 4;
+      store4<T>(out + c, v[i].x * rs * (1.f + s4[i].x) + h4[i].x, v[i].y * rs * (1.f + s4[i].y) + h4[i].y,
+                v[i].z * rs * (1.f + s4[i].z) + h4[i].z, v[i].w * rs * (1.f + s4[i].w) + h4[i].w);
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) v[i] = nv[i];
+    }
   }
 }
 
@@ -446,13 +471,15 @@ hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float
   if (nprob < 2) p1.rows = 0;
   const int rows = p[0].rows + p1.rows;
   if (rows == 0) return hipSuccess;
-  dim3 grid((rows + 3) / 4);
+  const int split0 = (p[0].rows + NORM_RW - 1) / NORM_RW * NORM_RW;
+  const int waves = split0 / NORM_RW + (p1.rows + NORM_RW - 1) / NORM_RW;
+  dim3 grid((waves + 3) / 4);
 #define NORM_CASE(g)                                                                                     \
   case g:                                                                                                \
     if (bf16_path)                                                                                       \
-      hipLaunchKernelGGL((norm_modulate_kernel<bf16, g>), grid, dim3(256), 0, stream, p[0], p1, eps);   \
+      hipLaunchKernelGGL((norm_modulate_kernel<bf16, g>), grid, dim3(256), 0, stream, p[0], p1, split0, eps);   \
     else                                                                                                 \
-      hipLaunchKernelGGL((norm_modulate_kernel<float, g>), grid, dim3(256), 0, stream, p[0], p1, eps);  \
+      hipLaunchKernelGGL((norm_modulate_kernel<float, g>), grid, dim3(256), 0, stream, p[0], p1, split0, eps);  \
     break;
   switch (D / 256) {
     NORM_CASE(1) NORM_CASE(2) NORM_CASE(3) NORM_CASE(4) NORM_CASE(5) NORM_CASE(6) NORM_CASE(7) NORM_CASE(8)
