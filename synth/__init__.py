@@ -129,7 +129,9 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
 def _draw(kind: str, shape, g: np.random.Generator, variant: str) -> np.ndarray:
     """One weight tensor.  'canonical': linear weights and biases N(0, 0.02),
     norm gains 1 + N(0, 0.02).  'wide': the same weights, but gains U(0.5, 1.5)
-    and biases N(0, 1), so gain and bias paths carry visible signal."""
+    and biases N(0, 1), so gain and bias paths carry visible signal.
+    'sharp': canonical, but norm gains 2.05 + N(0, 0.02): q.k logits about 4x
+    larger, so attention is sharp and its running max moves often."""
     if kind == "w":
         return g.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
     if kind == "b":
@@ -138,7 +140,8 @@ def _draw(kind: str, shape, g: np.random.Generator, variant: str) -> np.ndarray:
     if kind == "g":
         if variant == "wide":
             return g.uniform(0.5, 1.5, size=shape).astype(np.float32)
-        return np.float32(1.0) + g.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
+        base = np.float32(2.05) if variant == "sharp" else np.float32(1.0)
+        return base + g.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
     raise ValueError(kind)
 
 

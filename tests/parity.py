@@ -10,6 +10,12 @@ MAXABS_REL = 2e-2
 # x RMS(delta) against exact fp64 (emulated on the CPU at the storage points
 # the kernels use), so deltas are held to 5e-2 x RMS and the same cosine.
 DELTA_REL = 5e-2
+# Sharp attention (q/k RMSNorm gains near 2, logits ~4x the canonical ones):
+# the error of a logit from the bf16 rounding of q and k grows with the
+# logit, and the same CPU emulation gives max|err| ~0.043 x RMS(delta) for
+# the sharp test case (0.034 from rounding q and k alone, against 0.003 with
+# gains <= 1.5), so sharp cases are held to 8e-2.
+SHARP_DELTA_REL = 8e-2
 
 
 def stats(gpu, ref):

@@ -275,7 +275,8 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
     if (e != hipSuccess) return fail(LENS_ERR_HIP, "qk-norm/rope launch failed: %s", hipGetErrorString(e));
   }
   // 4. joint attention; outputs overwrite the (dead) norm outputs
-  AttnArgs aa{ws.Q, ws.K, ws.V, ws.a_img, ws.a_txt, txt_len, B, c->heads, Si, St, Sp, 0.125f};
+  AttnArgs aa{ws.Q, ws.K, ws.V, ws.a_img, ws.a_txt, txt_len, B, c->heads, Si, St, Sp, 0.125f,
+              {w->img.q_gain, w->img.k_gain, w->txt.q_gain, w->txt.k_gain}};
   {
     Timed t(LENS_KERNEL_ATTENTION, st);
     e = t.done(launch_attention(aa, bf, st));

@@ -66,6 +66,9 @@ __device__ __forceinline__ T *out_row(const AttnArgs &a, int b, int p) {
 // Lazy running max: rows rescale only when a tile's max exceeds the running
 // max by more than TAU (log2 units), so probabilities stay <= 2^TAU.
 constexpr float TAU = 8.0f;
+// largest score bound used as a fixed max: p >= 2^(-2 BOUND_MAX) keeps
+// probabilities and row sums far above fp32 / bf16 underflow
+constexpr float BOUND_MAX = 48.0f;
 
 // -------------------------------------------------------------- bf16
 // K and V^T tiles arrive by direct
@@ -119,7 +122,10 @@ __device__ __forceinline__ bf16x8 v_frag(const char *sVb, int ks, int dh, int la
 // minit = -m (16 copies), so the MFMAs deliver s - m directly and p = exp2(.)
 // needs no subtraction; only when a tile's max exceeds m by more than TAU
 // is m raised (O and l rescaled, this tile's values shifted).
-template <bool FIRST, bool MASK>
+//   BOUNDED: every score is known to be <= m = -minit[0] (a bound from the
+//   q/k gains, see attn_bf16), so the max tracking and rescaling are skipped;
+//   the QK MFMAs start from -m on every tile.
+template <bool FIRST, bool MASK, bool BOUNDED>
 __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, const bf16x8 (&qf)[4], f32x16 (&o)[2],
                                              float &m_run, float &l_run, f32x16 &minit, int kv0, int n_kv, int ql,
                                              int hl) {
@@ -131,7 +137,7 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
     const int slot = (hl ^ sw) << 4;
     const bf16x8 k0 = *(const bf16x8 *)(sKb + ql * 128 + slot);
     const bf16x8 k1 = *(const bf16x8 *)(sKb + (32 + ql) * 128 + slot);
-    const f32x16 c0 = FIRST ? f32x16{} : minit;
+    const f32x16 c0 = (FIRST && !BOUNDED) ? f32x16{} : minit;
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], c0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[0], c0, 0, 0, 0);
   }
@@ -151,6 +157,7 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
       if (kv + 32 >= n_kv) s1[r] = -INFINITY;
     }
   }
+  if constexpr (!BOUNDED) {
   float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
@@ -179,6 +186,7 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
         minit[r] = -m_run;
       }
     }
+  }
   }
   bf16x8 pb[4];
   float lsum = 0.f;
@@ -254,6 +262,27 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
                                      16, 0, 0);                                                             \
   } while (0)
 
+  // Score bound: q and k are RMS-normalised per head (norm < 8 before the
+  // gain), scaled by at most max|gain|, rotated (norm kept) and q is scaled
+  // by log2(e) / 8, so |s| <= 8 log2(e) max|g_q| max|g_k| over both
+  // streams' gains; the margin covers the bf16 rounding of q and k.  With
+  // the bound as the subtracted max, p = exp2(s - m) needs no running max
+  // (softmax does not depend on the constant) as long as 2^(-2m) stays far
+  // from fp32 underflow, i.e. m <= BOUND_MAX; otherwise the online max runs.
+  float m_bound = INFINITY;
+  if (a.gain[0] && a.gain[1] && a.gain[2] && a.gain[3]) {
+    const float gq = fmaxf(fabsf((float)((const bf16 *)a.gain[0])[lane]), fabsf((float)((const bf16 *)a.gain[2])[lane]));
+    const float gk = fmaxf(fabsf((float)((const bf16 *)a.gain[1])[lane]), fabsf((float)((const bf16 *)a.gain[3])[lane]));
+    float mq = gq, mk = gk;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) {
+      mq = fmaxf(mq, __shfl_xor(mq, sh));
+      mk = fmaxf(mk, __shfl_xor(mk, sh));
+    }
+    m_bound = __uint_as_float(
+        __builtin_amdgcn_readfirstlane(__float_as_uint(8.0f * 1.4426950408889634f * mq * mk * 1.02f + 0.02f)));
+  }
+
   f32x16 o[2] = {f32x16{}, f32x16{}};
   f32x16 minit;
   float m_run = 0.f, l_run = 0.f;
@@ -262,25 +291,37 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   wait_vmcnt0();
   __builtin_amdgcn_s_barrier();
   if (1 < n_tiles) ATT_ISSUE(1);
-  if (n_full >= 1)
-    attn_tile<true, false>(smem, smem + TILE_BYTES, qf, o, m_run, l_run, minit, 0, n_kv, ql, hl);
-  else
-    attn_tile<true, true>(smem, smem + TILE_BYTES, qf, o, m_run, l_run, minit, 0, n_kv, ql, hl);
-  for (int t = 1; t < n_full; ++t) {
-    wait_vmcnt0();      // this wave's part of tile t has landed
-    wait_lgkmcnt0();    // and its reads of tile t - 1 have returned
-    __builtin_amdgcn_s_barrier();
-    if (t + 1 < n_tiles) ATT_ISSUE(t + 1);
-    const char *sb = smem + (t & 1) * STAGE;
-    attn_tile<false, false>(sb, sb + TILE_BYTES, qf, o, m_run, l_run, minit, t * KV_T, n_kv, ql, hl);
+#define ATT_TILES(BND)                                                                                      \
+  do {                                                                                                      \
+    if (n_full >= 1)                                                                                        \
+      attn_tile<true, false, BND>(smem, smem + TILE_BYTES, qf, o, m_run, l_run, minit, 0, n_kv, ql, hl);    \
+    else                                                                                                    \
+      attn_tile<true, true, BND>(smem, smem + TILE_BYTES, qf, o, m_run, l_run, minit, 0, n_kv, ql, hl);     \
+    for (int t = 1; t < n_full; ++t) {                                                                      \
+      wait_vmcnt0();   /* this wave's part of tile t has landed */                                         \
+      wait_lgkmcnt0(); /* and its reads of tile t - 1 have returned */                                     \
+      __builtin_amdgcn_s_barrier();                                                                         \
+      if (t + 1 < n_tiles) ATT_ISSUE(t + 1);                                                                \
+      const char *sb = smem + (t & 1) * STAGE;                                                              \
+      attn_tile<false, false, BND>(sb, sb + TILE_BYTES, qf, o, m_run, l_run, minit, t * KV_T, n_kv, ql, hl); \
+    }                                                                                                       \
+    if (n_full < n_tiles && n_full >= 1) {                                                                  \
+      wait_vmcnt0();                                                                                        \
+      wait_lgkmcnt0();                                                                                      \
+      __builtin_amdgcn_s_barrier();                                                                         \
+      const char *sb = smem + (n_full & 1) * STAGE;                                                         \
+      attn_tile<false, true, BND>(sb, sb + TILE_BYTES, qf, o, m_run, l_run, minit, n_full * KV_T, n_kv, ql,  \
+                                  hl);                                                                      \
+    }                                                                                                       \
+  } while (0)
+  if (m_bound <= BOUND_MAX) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) minit[r] = -m_bound;
+    ATT_TILES(true);
+  } else {
+    ATT_TILES(false);
   }
-  if (n_full < n_tiles && n_full >= 1) {
-    wait_vmcnt0();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    const char *sb = smem + (n_full & 1) * STAGE;
-    attn_tile<false, true>(sb, sb + TILE_BYTES, qf, o, m_run, l_run, minit, n_full * KV_T, n_kv, ql, hl);
-  }
+#undef ATT_TILES
 #undef ATT_ISSUE
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);

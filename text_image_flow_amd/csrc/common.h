@@ -88,6 +88,9 @@ struct AttnArgs {
   const int32_t *txt_len;  // device, [B] or NULL
   int32_t B, H, S_img, S_txt, S_pad;
   float scale;             // 1/sqrt(head_dim)
+  // bf16 path: the [64] q/k RMSNorm gains of both streams (q_img, k_img,
+  // q_txt, k_txt), from which the kernel bounds every score; NULL: no bound
+  const void *gain[4];
 };
 hipError_t launch_attention(const AttnArgs &a, bool bf16_path, hipStream_t stream);
 
