@@ -71,15 +71,24 @@ constexpr float TAU = 8.0f;
 constexpr float BOUND_MAX = 48.0f;
 
 // -------------------------------------------------------------- bf16
-// K and V^T tiles arrive by direct
-// global->LDS loads (global_load_lds_dwordx4: one wave instruction fills 1 KB
-// = 8 rows of 128 bytes) into a double-buffered ring, so no VGPRs stage
-// them.  Rows are unpadded; 16-byte chunk c of row r sits in slot
+// K and V tiles arrive by direct global->LDS loads (raw buffer loads with
+// the lds bit: one wave instruction fills 1 KB = 8 rows of 128 bytes) into
+// a double-buffered ring, so no VGPRs stage them; each lane keeps a
+// constant 32-bit offset inside the (sample, head) slice and the tile's
+// offset rides in the scalar offset, so a tile's loads need no vector
+// address arithmetic.  Rows are unpadded; 16-byte chunk c of row r sits in slot
 // c ^ ((r >> 1) & 7): the 16 lanes that one LDS cycle serves read 16
 // consecutive rows, and these land on 16 distinct 16-byte bank groups of the
 // 64 banks (a plain c ^ (r & 7) maps rows r and r + 8 onto the same group).
 // The partial last tile is peeled so the steady-state loop carries no mask.
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from base + voff + soff into LDS at M0 + 16 * lane
+// (bounds: bytes)
+__device__ __forceinline__ void buffer_lds16(const void *base, int bytes, lds_void_t *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, bytes, 0x00020000),
+                                           dst, 16, voff, soff, 0, 0);
+}
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
@@ -189,7 +198,7 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
   }
   }
   bf16x8 pb[4];
-  float lsum = 0.f;
+  float lsum = l_run;   // the row sum continues the running sum directly
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
     bf16x2 p0 = {(bf16)__builtin_amdgcn_exp2f(s0[e]), (bf16)__builtin_amdgcn_exp2f(s0[e + 1])};
@@ -205,7 +214,7 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
     pb[2][e] = p2[0]; pb[2][e + 1] = p2[1];
     pb[3][e] = p3[0]; pb[3][e + 1] = p3[1];
   }
-  l_run += lsum;
+  l_run = lsum;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const bf16x8 v0 = v_frag(sVb, ks, 0, vlane);
@@ -223,7 +232,8 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   const int S = a.S_img + a.S_txt;
   int qb, h, b;
   attn_block_coords((S + 127) / 128, a.H, qb, h, b);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = qb * 128 + wave * 32;
   const int64_t bh = (int64_t)b * a.H + h;
   const bf16 *Qg = (const bf16 *)a.Q + bh * a.S_pad * 64;
@@ -245,21 +255,20 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   // each wave fills rows [wave * 16, wave * 16 + 16) of the K and V tiles:
   // two instructions of 8 rows each; lane -> row + lane / 8, slot lane % 8
   const int r0 = wave * 16 + (lane >> 3), r1 = r0 + 8, slot = lane & 7;
-  const bf16 *k_src0 = Kg + (int64_t)r0 * 64 + ((slot ^ ((r0 >> 1) & 7)) * 8);
-  const bf16 *k_src1 = Kg + (int64_t)r1 * 64 + ((slot ^ ((r1 >> 1) & 7)) * 8);
-  const bf16 *v_src0 = Vg + (int64_t)r0 * 64 + ((slot ^ vswz(r0)) * 8);
-  const bf16 *v_src1 = Vg + (int64_t)r1 * 64 + ((slot ^ vswz(r1)) * 8);
+  const int k_off0 = r0 * 128 + ((slot ^ ((r0 >> 1) & 7)) * 16);
+  const int k_off1 = r1 * 128 + ((slot ^ ((r1 >> 1) & 7)) * 16);
+  const int v_off0 = r0 * 128 + ((slot ^ vswz(r0)) * 16);
+  const int v_off1 = r1 * 128 + ((slot ^ vswz(r1)) * 16);
+  const int slice_bytes = a.S_pad * 128;      // one (sample, head) slice of K or V
   const int dst0 = wave * 16 * 128, dst1 = dst0 + 8 * 128;
-#define ATT_ISSUE(t_)                                                                                       \
+#define ATT_ISSUE(t_, stage_)                                                                               \
   do {                                                                                                      \
-    char *sb_ = smem + ((t_) & 1) * STAGE;                                                                  \
-    const int64_t ko_ = (int64_t)(t_) * KV_T * 64, vo_ = ko_;                                              \
-    __builtin_amdgcn_global_load_lds((const void *)(k_src0 + ko_), (lds_void_t *)(sb_ + dst0), 16, 0, 0);  \
-    __builtin_amdgcn_global_load_lds((const void *)(k_src1 + ko_), (lds_void_t *)(sb_ + dst1), 16, 0, 0);  \
-    __builtin_amdgcn_global_load_lds((const void *)(v_src0 + vo_), (lds_void_t *)(sb_ + TILE_BYTES + dst0), \
-                                     16, 0, 0);                                                             \
-    __builtin_amdgcn_global_load_lds((const void *)(v_src1 + vo_), (lds_void_t *)(sb_ + TILE_BYTES + dst1), \
-                                     16, 0, 0);                                                             \
+    char *sb_ = smem + (stage_) * STAGE;                                                                    \
+    const int so_ = (t_) * KV_T * 128;                                                                      \
+    buffer_lds16(Kg, slice_bytes, (lds_void_t *)(sb_ + dst0), k_off0, so_);                                \
+    buffer_lds16(Kg, slice_bytes, (lds_void_t *)(sb_ + dst1), k_off1, so_);                                \
+    buffer_lds16(Vg, slice_bytes, (lds_void_t *)(sb_ + TILE_BYTES + dst0), v_off0, so_);                   \
+    buffer_lds16(Vg, slice_bytes, (lds_void_t *)(sb_ + TILE_BYTES + dst1), v_off1, so_);                   \
   } while (0)
 
   // Score bound: q and k are RMS-normalised per head (norm < 8 before the
@@ -286,25 +295,37 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   f32x16 o[2] = {f32x16{}, f32x16{}};
   f32x16 minit;
   float m_run = 0.f, l_run = 0.f;
-  ATT_ISSUE(0);
+  ATT_ISSUE(0, 0);
   // tile 0 (always holds image keys, so at least one valid key per row)
   wait_vmcnt0();
   __builtin_amdgcn_s_barrier();
-  if (1 < n_tiles) ATT_ISSUE(1);
+  if (1 < n_tiles) ATT_ISSUE(1, 1);
+// one full tile t held in stage st_ (= t & 1): wait for this wave's part of
+// it, and for its own reads of tile t - 1, then the barrier frees stage
+// 1 - st_ for tile t + 1
+#define ATT_STEP(t_, st_, BND)                                                                              \
+  do {                                                                                                      \
+    wait_vmcnt0();                                                                                          \
+    wait_lgkmcnt0();                                                                                        \
+    __builtin_amdgcn_s_barrier();                                                                           \
+    if ((t_) + 1 < n_tiles) ATT_ISSUE((t_) + 1, 1 - (st_));                                                 \
+    const char *sb_ = smem + (st_) * STAGE;                                                                 \
+    attn_tile<false, false, BND>(sb_, sb_ + TILE_BYTES, qf, o, m_run, l_run, minit, (t_) * KV_T, n_kv, ql, hl); \
+  } while (0)
 #define ATT_TILES(BND)                                                                                      \
   do {                                                                                                      \
     if (n_full >= 1)                                                                                        \
       attn_tile<true, false, BND>(smem, smem + TILE_BYTES, qf, o, m_run, l_run, minit, 0, n_kv, ql, hl);    \
     else                                                                                                    \
       attn_tile<true, true, BND>(smem, smem + TILE_BYTES, qf, o, m_run, l_run, minit, 0, n_kv, ql, hl);     \
-    for (int t = 1; t < n_full; ++t) {                                                                      \
-      wait_vmcnt0();   /* this wave's part of tile t has landed */                                         \
-      wait_lgkmcnt0(); /* and its reads of tile t - 1 have returned */                                     \
-      __builtin_amdgcn_s_barrier();                                                                         \
-      if (t + 1 < n_tiles) ATT_ISSUE(t + 1);                                                                \
-      const char *sb = smem + (t & 1) * STAGE;                                                              \
-      attn_tile<false, false, BND>(sb, sb + TILE_BYTES, qf, o, m_run, l_run, minit, t * KV_T, n_kv, ql, hl); \
+    /* two tiles per trip: odd tiles sit in stage 1, even ones in stage 0, */                               \
+    /* so every LDS address is a fixed offset from a loop-invariant base */                                 \
+    int t = 1;                                                                                              \
+    for (; t + 1 < n_full; t += 2) {                                                                        \
+      ATT_STEP(t, 1, BND);                                                                                  \
+      ATT_STEP(t + 1, 0, BND);                                                                              \
     }                                                                                                       \
+    if (t < n_full) ATT_STEP(t, 1, BND);                                                                    \
     if (n_full < n_tiles && n_full >= 1) {                                                                  \
       wait_vmcnt0();                                                                                        \
       wait_lgkmcnt0();                                                                                      \
@@ -322,6 +343,7 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
     ATT_TILES(false);
   }
 #undef ATT_TILES
+#undef ATT_STEP
 #undef ATT_ISSUE
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
