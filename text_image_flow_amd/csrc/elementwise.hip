@@ -294,72 +294,107 @@ hipError_t gemv_run(const GemvBatch &g, const float *x, int K, bool silu_in, hip
   return hipGetLastError();
 }
 
-// bf16 weights: the block stages f(x) for all its samples in LDS once (the
-// four waves share it; f is SiLU when silu_in), each wave keeps its k-range
-// of f(x) in registers and walks GEMV_RW rows, 8 at a time, with the 8 rows'
-// 16-byte loads for all KC k-chunks in flight together.  Long-lived waves
-// amortise the staging; KC = ceil(K / 512) sizes the register arrays.
-constexpr int GEMV_RW = 64;       // rows per wave
+// bf16 weights: a persistent grid (GEMV_BLOCKS_PER_CU blocks per CU) walks
+// the rows of all problems of the batch as one index space, each wave a
+// contiguous run of rows, so no tail of half-empty rounds is left.  The
+// block stages f(x) for all its samples in LDS once (f is SiLU when
+// silu_in).  A wave takes GEMV_RG rows at a time with their 16-byte weight
+// loads for all KC k-chunks (lane l owns k = 512 c + 8 l .. + 7) in flight
+// together; f(x) comes from LDS as it is used, so few VGPRs are live and
+// several waves fit per SIMD.  The RG x NB lane partials are reduced by a
+// transposing butterfly: every exchange step halves the values a lane
+// holds, so the sums cost about RG x NB shuffles instead of 6 each.
+constexpr int GEMV_RG = 4;               // rows per group (loads in flight together)
+constexpr int GEMV_BLOCKS_PER_CU = 4;
+
+template <int N>
+struct pow2_ceil { static constexpr int v = N <= 1 ? 1 : 2 * pow2_ceil<(N + 1) / 2>::v; };
+template <>
+struct pow2_ceil<1> { static constexpr int v = 1; };
 
 template <int NB, int KC>
-__global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvBatch g, const float *x, int K, int silu_in) {
-  __shared__ float sx[NB * GEMV_MAXK];
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvBatch g, const float *x, int K, int silu_in,
+                                                        int total_rows, int rows_per_wave) {
+  __shared__ __attribute__((aligned(16))) float sx[NB * GEMV_MAXK];
   for (int i = threadIdx.x; i < NB * K; i += 256) {
     const float v = x[i];
     sx[i] = silu_in ? silu_f(v) : v;
   }
   __syncthreads();
-  const int prob = blockIdx.y;
-  const int N = g.N[prob];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rowb = (blockIdx.x * GEMV_WAVES + wave) * GEMV_RW;
-  if (rowb >= N) return;
-  float fx[NB][KC][8];
-#pragma unroll
-  for (int c = 0; c < KC; ++c)
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = c * 512 + lane * 8 + e;
-        fx[b][c][e] = k < K ? sx[b * K + k] : 0.f;
-      }
-  const bf16 *W = (const bf16 *)g.W[prob];
-  const bf16 *bias = (const bf16 *)g.bias[prob];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r_begin = (blockIdx.x * GEMV_WAVES + wave) * rows_per_wave;
+  const int r_end = min(total_rows, r_begin + rows_per_wave);
+  if (r_begin >= r_end) return;
+  // problem of the wave's first row
+  int prob = 0, pbase = 0;
+  while (prob + 1 < g.nprob && r_begin >= pbase + g.N[prob]) pbase += g.N[prob++];
+  constexpr int NV = GEMV_RG * NB, VP = pow2_ceil<NV>::v;
+  static_assert(VP <= 64, "values per lane");
 #pragma unroll 1
-  for (int rg = 0; rg < GEMV_RW; rg += GEMV_ROWS) {
-    const int row0 = rowb + rg;
-    if (row0 >= N) break;
-    bf16x8 wv[KC][GEMV_ROWS];
+  for (int r0 = r_begin; r0 < r_end; r0 += GEMV_RG) {
+    // each row's problem and row inside it (rows past the run repeat the last)
+    int rp[GEMV_RG], rn[GEMV_RG];
+#pragma unroll
+    for (int r = 0; r < GEMV_RG; ++r) {
+      const int row = min(r0 + r, r_end - 1);
+      while (prob + 1 < g.nprob && row >= pbase + g.N[prob]) pbase += g.N[prob++];
+      rp[r] = prob;
+      rn[r] = row - pbase;
+    }
+    bf16x8 wv[KC][GEMV_RG];
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const int k = c * 512 + lane * 8;
 #pragma unroll
-      for (int r = 0; r < GEMV_ROWS; ++r) {
-        const int n = row0 + r < N ? row0 + r : N - 1;
-        wv[c][r] = k < K ? *(const bf16x8 *)(W + (int64_t)n * K + k) : bf16x8{};
-      }
+      for (int r = 0; r < GEMV_RG; ++r)
+        wv[c][r] = k < K ? *(const bf16x8 *)((const bf16 *)g.W[rp[r]] + (int64_t)rn[r] * K + k) : bf16x8{};
     }
-    float acc[GEMV_ROWS][NB];
+    float v[VP];
 #pragma unroll
-    for (int r = 0; r < GEMV_ROWS; ++r)
+    for (int i = 0; i < VP; ++i) v[i] = 0.f;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-#pragma unroll
-      for (int r = 0; r < GEMV_ROWS; ++r)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[r][b] = fmaf((float)wv[c][r][e], fx[b][c][e], acc[r][b]);
-#pragma unroll
-    for (int r = 0; r < GEMV_ROWS; ++r) {
-      const int n = row0 + r;
+    for (int c = 0; c < KC; ++c) {
+      const int k = c * 512 + lane * 8;
+      if (k >= K) break;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float v = wave_sum(acc[r][b]);
-        if (lane == 0 && n < N) g.y[prob][(int64_t)b * g.y_stride[prob] + n] = v + (bias ? (float)bias[n] : 0.f);
+        const float4 x0 = *(const float4 *)(sx + b * K + k), x1 = *(const float4 *)(sx + b * K + k + 4);
+        const float xf[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int r = 0; r < GEMV_RG; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[r * NB + b] = fmaf((float)wv[c][r][e], xf[e], v[r * NB + b]);
+      }
+    }
+    // transposing butterfly: at the step with offset o a lane keeps the
+    // upper or lower half of its values (by lane bit o), each summed with
+    // its partner's copy
+    int o = 32;
+#pragma unroll
+    for (int cnt = VP; cnt > 1; cnt >>= 1) {
+      const bool hi = lane & o;
+#pragma unroll
+      for (int i = 0; i < cnt / 2; ++i) {
+        const float send = hi ? v[i] : v[i + cnt / 2];
+        const float keep = hi ? v[i + cnt / 2] : v[i];
+        v[i] = keep + __shfl_xor(send, o);
+      }
+      o >>= 1;
+    }
+    for (int oo = o; oo >= 1; oo >>= 1) v[0] += __shfl_xor(v[0], oo);
+    // now every aligned group of 2 o lanes holds one full sum; its index is
+    // the sum of the halves kept (VP / 2 for lane bit 32, VP / 4 for 16, ...)
+    if ((lane & (2 * o - 1)) == 0) {
+      int idx = 0, w = VP / 2;
+#pragma unroll
+      for (int oo = 32; oo > o; oo >>= 1, w >>= 1) idx += (lane & oo) ? w : 0;
+      if (idx < NV) {
+        const int r = idx / NB, b = idx - r * NB;
+        if (r0 + r < r_end) {
+          const bf16 *bias = (const bf16 *)g.bias[rp[r]];
+          g.y[rp[r]][(int64_t)b * g.y_stride[rp[r]] + rn[r]] = v[0] + (bias ? (float)bias[rn[r]] : 0.f);
+        }
       }
     }
   }
@@ -367,11 +402,20 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvBatch g, const float
 
 template <int NB, int KC>
 hipError_t gemv_bf16_run(const GemvBatch &g, const float *x, int K, bool silu_in, hipStream_t st) {
-  int maxN = 0;
-  for (int i = 0; i < g.nprob; ++i) maxN = g.N[i] > maxN ? g.N[i] : maxN;
-  const int rows_per_block = GEMV_WAVES * GEMV_RW;
-  dim3 grid((maxN + rows_per_block - 1) / rows_per_block, g.nprob);
-  hipLaunchKernelGGL((gemv_bf16_kernel<NB, KC>), grid, dim3(256), 0, st, g, x, K, silu_in ? 1 : 0);
+  int total = 0;
+  for (int i = 0; i < g.nprob; ++i) total += g.N[i];
+  if (total <= 0) return hipSuccess;
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus = c;
+  }
+  const int waves = cus * GEMV_BLOCKS_PER_CU * GEMV_WAVES;
+  int rpw = (total + waves - 1) / waves;
+  rpw = ((rpw + GEMV_RG - 1) / GEMV_RG) * GEMV_RG;
+  const int blocks = (total + rpw * GEMV_WAVES - 1) / (rpw * GEMV_WAVES);
+  hipLaunchKernelGGL((gemv_bf16_kernel<NB, KC>), dim3(blocks), dim3(256), 0, st, g, x, K, silu_in ? 1 : 0, total, rpw);
   return hipGetLastError();
 }
 
