@@ -322,6 +322,27 @@ def flow_step(x, v_cond, v_uncond, dt, scale):
     return euler_step(x, v, dt)
 
 
+def cfg_combine_rescaled(v_cond, v_uncond, scale):
+    """Norm-rescaled CFG ([blog] "Exploring Image Editing": Lens's inference
+    rescales the guided velocity by norms; the printed formula keeps only the
+    plain combination).  READING: per token (the last axis, the 128 latent
+    channels of a patch token), comb = u + s (c - u), then
+    comb <- comb * ||c|| / ||comb||, so the guided velocity keeps the
+    conditional velocity's per-token norm.  A token with ||comb|| = 0 keeps
+    comb (= 0)."""
+    vc = _f(v_cond)
+    comb = vc if v_uncond is None else cfg_combine(v_cond, v_uncond, scale)
+    nc = np.sqrt(np.sum(vc * vc, axis=-1, keepdims=True))
+    nb = np.sqrt(np.sum(comb * comb, axis=-1, keepdims=True))
+    factor = np.where(nb > 0.0, nc / np.where(nb > 0.0, nb, 1.0), 1.0)
+    return comb * factor
+
+
+def flow_step_rescaled(x, v_cond, v_uncond, dt, scale):
+    """Norm-rescaled CFG combine then the Euler update (x, v: [..., C])."""
+    return euler_step(x, cfg_combine_rescaled(v_cond, v_uncond, scale), dt)
+
+
 def sample(velocity, x0, steps, scale=1.0, use_uncond=False):
     """Euler loop over time_grid(steps).  velocity(x, t) returns v_cond, or
     (v_cond, v_uncond) when use_uncond; returns the final x (float64)."""
@@ -344,5 +365,5 @@ __all__ = [
     "linear", "silu", "rms_norm", "adaln", "modulate", "rope_angles", "rope", "attention",
     "swiglu_mlp", "block_forward", "timestep_features", "timestep_embedding", "text_embed",
     "final_layer", "dit_forward", "time_grid", "cfg_combine", "euler_step", "flow_step",
-    "sample", "stream_param_count",
+    "cfg_combine_rescaled", "flow_step_rescaled", "sample", "stream_param_count",
 ]

@@ -484,3 +484,45 @@ def test_euler_linear_path_is_exact():
     x0c, x0u, x1 = rs.standard_normal(30), rs.standard_normal(30), rs.standard_normal(30)
     x = O.sample(lambda x, t: (x1 - x0c, x1 - x0u), x1, 7, scale=5.0, use_uncond=True)
     np.testing.assert_allclose(x, x0u + 5.0 * (x0c - x0u), atol=1e-12)
+
+
+# ------------------------------------------------------------ norm-rescaled CFG
+def test_rescaled_cfg_worked_example():
+    """c = (3, 4), u = 0, s = 2: comb = (6, 8) with norm 10, rescaled to the
+    conditional norm 5 -> (3, 4); a second token with u = c stays c."""
+    c = np.array([[3.0, 4.0], [1.0, -2.0]])
+    u = np.array([[0.0, 0.0], [1.0, -2.0]])
+    np.testing.assert_allclose(O.cfg_combine_rescaled(c, u, 2.0), [[3.0, 4.0], [1.0, -2.0]], atol=1e-15)
+    # direction comes from the combination, length from c
+    c2 = np.array([[1.0, 0.0]])
+    u2 = np.array([[0.0, 1.0]])
+    out = O.cfg_combine_rescaled(c2, u2, 3.0)          # comb = (3, -2)
+    np.testing.assert_allclose(out, np.array([[3.0, -2.0]]) / math.sqrt(13.0), atol=1e-15)
+
+
+def test_rescaled_cfg_properties():
+    rs = np.random.default_rng(3)
+    c, u = rs.standard_normal((5, 7, 128)), rs.standard_normal((5, 7, 128))
+    # s = 1: comb = c (up to rounding), so the rescale factor is 1
+    np.testing.assert_allclose(O.cfg_combine_rescaled(c, u, 1.0), c, atol=1e-13)
+    for s in (0.0, 2.5, 5.0):
+        out = O.cfg_combine_rescaled(c, u, s)
+        # per-token norm equals the conditional norm
+        np.testing.assert_allclose(np.linalg.norm(out, axis=-1), np.linalg.norm(c, axis=-1), rtol=1e-12)
+        # per-token direction equals the plain guided direction
+        comb = O.cfg_combine(c, u, s)
+        cosv = np.sum(out * comb, -1) / (np.linalg.norm(out, axis=-1) * np.linalg.norm(comb, axis=-1))
+        np.testing.assert_allclose(cosv, 1.0, atol=1e-12)
+    # no uncond: identity
+    np.testing.assert_array_equal(O.cfg_combine_rescaled(c, None, 5.0), c)
+
+
+def test_rescaled_cfg_zero_norm_token_and_euler():
+    c = np.array([[1.0, 1.0], [2.0, 0.0]])
+    u = np.array([[1.25, 1.25], [0.0, 0.0]])
+    # token 0: s = 5 gives comb = 1.25 + 5 (1 - 1.25) = 0 exactly -> kept at 0
+    out = O.cfg_combine_rescaled(c, u, 5.0)
+    np.testing.assert_array_equal(out[0], [0.0, 0.0])
+    np.testing.assert_allclose(out[1], [2.0, 0.0], atol=1e-15)   # comb = (10, 0) rescaled to norm 2
+    x = np.array([[0.5, -0.5], [1.0, 1.0]])
+    np.testing.assert_allclose(O.flow_step_rescaled(x, c, u, -0.25, 5.0), x - 0.25 * out, atol=1e-15)
