@@ -295,12 +295,32 @@ def dit_forward(top, blocks, x, txt_feats, t, img_pos, txt_pos, txt_len=None, *,
 # sampler
 # --------------------------------------------------------------------------
 
-def time_grid(steps):
+def time_grid(steps, mu=None):
     """t_k = 1 - k/N, k = 0..N.  [paper] 前置知识 (Flow Matching): the path
     x_t = (1 - t) x0 + t x1 with target x1 - x0, so t = 1 is the noise end
     when x1 is noise and sampling starts from N(0, 1) latents.  READING: a
-    uniform grid, no resolution shift."""
-    return 1.0 - np.arange(steps + 1, dtype=F64) / steps
+    uniform grid; with mu, each point is moved by time_shift(t, mu)."""
+    t = 1.0 - np.arange(steps + 1, dtype=F64) / steps
+    return t if mu is None else time_shift(t, mu)
+
+
+def time_shift(t, mu):
+    """Resolution-dependent timestep shift ([paper] 前置知识 and 方法步骤详情:
+    logit-normal timesteps with a location mu(n) interpolated linearly in
+    the token count, mu = 1.06 for the 512^2 stage).  READING: the inference
+    grid is shifted by the same mu as t' = e^mu t / (e^mu t + 1 - t), i.e. a
+    translation by mu in logit space; t = 0 and t = 1 stay fixed."""
+    t = _f(t)
+    e = math.exp(mu)
+    return e * t / (e * t + 1.0 - t)
+
+
+def mu_for_tokens(n, n0, mu0, n1, mu1):
+    """mu(n) on the straight line through (n0, mu0) and (n1, mu1) ([paper]
+    方法步骤详情: linear interpolation in the token count).  The pages give
+    one point only (mu = 1.06 at 512^2, 1024 tokens); the other is the
+    caller's."""
+    return mu0 + (float(n) - n0) * (mu1 - mu0) / (n1 - n0)
 
 
 def cfg_combine(v_cond, v_uncond, scale):
@@ -365,5 +385,5 @@ __all__ = [
     "linear", "silu", "rms_norm", "adaln", "modulate", "rope_angles", "rope", "attention",
     "swiglu_mlp", "block_forward", "timestep_features", "timestep_embedding", "text_embed",
     "final_layer", "dit_forward", "time_grid", "cfg_combine", "euler_step", "flow_step",
-    "cfg_combine_rescaled", "flow_step_rescaled", "sample", "stream_param_count",
+    "cfg_combine_rescaled", "flow_step_rescaled", "time_shift", "mu_for_tokens", "sample", "stream_param_count",
 ]

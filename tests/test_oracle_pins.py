@@ -526,3 +526,27 @@ def test_rescaled_cfg_zero_norm_token_and_euler():
     np.testing.assert_allclose(out[1], [2.0, 0.0], atol=1e-15)   # comb = (10, 0) rescaled to norm 2
     x = np.array([[0.5, -0.5], [1.0, 1.0]])
     np.testing.assert_allclose(O.flow_step_rescaled(x, c, u, -0.25, 5.0), x - 0.25 * out, atol=1e-15)
+
+
+# ------------------------------------------------------------ timestep shift
+def test_time_shift_is_a_logit_translation():
+    t = np.linspace(0.0, 1.0, 41)[1:-1]
+    for mu in (-0.7, 0.5, 1.06, 2.0):
+        ts = O.time_shift(t, mu)
+        np.testing.assert_allclose(scipy.special.logit(ts), scipy.special.logit(t) + mu, atol=1e-12)
+        assert np.all(np.diff(ts) > 0)                                      # order kept
+        np.testing.assert_allclose(O.time_shift(ts, -mu), t, atol=1e-14)    # -mu undoes mu
+    np.testing.assert_array_equal(O.time_shift(np.array([0.0, 1.0]), 1.06), [0.0, 1.0])
+    np.testing.assert_allclose(O.time_shift(t, 0.0), t, rtol=0, atol=1e-15)   # identity up to rounding
+    assert abs(O.time_shift(0.5, 1.06) - scipy.special.expit(1.06)) < 1e-15
+
+
+def test_shifted_grid_and_mu_line():
+    ts = O.time_grid(20, mu=1.06)
+    assert ts[0] == 1.0 and ts[-1] == 0.0 and np.all(np.diff(ts) < 0)
+    np.testing.assert_allclose(ts, O.time_shift(O.time_grid(20), 1.06), rtol=0, atol=0)
+    # a positive shift spends more of the steps at high noise
+    assert np.all(ts[1:-1] > O.time_grid(20)[1:-1])
+    assert O.mu_for_tokens(1024, 1024, 1.06, 4096, 1.5) == 1.06
+    assert abs(O.mu_for_tokens(4096, 1024, 1.06, 4096, 1.5) - 1.5) < 1e-15
+    assert abs(O.mu_for_tokens(2560, 1024, 1.06, 4096, 1.5) - 1.28) < 1e-12
