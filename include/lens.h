@@ -173,6 +173,26 @@ lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond,
                            float cfg_scale, void *x_lowp_out, lens_dtype lowp_dtype, void *hip_stream);
 
 /*
+ * Flow-matching Euler step with norm-rescaled classifier-free guidance, on
+ * n_tokens tokens of `channels` contiguous f32 elements each (the latent
+ * token layout [.., S_img, out_ch] of v_out: channels = out_ch).  Per token:
+ *   comb = v_uncond + cfg_scale (v_cond - v_uncond)   (comb = v_cond when
+ *          v_uncond is NULL),
+ *   comb <- comb * ||v_cond|| / ||comb||               (unchanged where
+ *          ||comb|| = 0; 2-norms over the token's channels),
+ *   x <- x + dt comb.
+ * Source: Lens blog (zjwfufu.github.io), "Exploring Image Editing": Lens's
+ * inference uses a norm-rescaled CFG; the page prints only the combination,
+ * and the rescale of each token to the conditional norm is the reading
+ * taken here.  x is updated in place; x_lowp_out and lowp_dtype as for
+ * lens_flow_step.  Requires n_tokens >= 0, channels >= 1; x, v_cond and
+ * v_uncond must not overlap x_lowp_out.
+ */
+lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *v_uncond, int64_t n_tokens,
+                                    int32_t channels, float dt, float cfg_scale, void *x_lowp_out,
+                                    lens_dtype lowp_dtype, void *hip_stream);
+
+/*
  * Opt-in kernel timer for measurement.  lens_timer_start(mask) makes every
  * later launch of the kernel families whose bit (1 << lens_kernel_kind) is
  * set record a pair of HIP events around itself, on the stream it is

@@ -6,6 +6,7 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 import text_image_flow_amd as T
@@ -119,6 +120,12 @@ def test_dit_and_flow_argument_checks():
     assert T.lens_flow_step(None, None, None, 5, 0.1, 1.0, None, 1, None) == L.LENS_ERR_INVALID_ARG
     assert T.lens_flow_step(0x1000, 0x1000, None, 5, 0.1, 1.0, 0x1000, 9, None) == L.LENS_ERR_INVALID_ARG
     assert T.lens_flow_step(None, None, None, 0, 0.1, 1.0, None, 1, None) == L.LENS_OK   # empty: nothing to do
+    R = T.lens_flow_step_rescaled
+    assert R(None, None, None, -1, 128, 0.1, 1.0, None, 1, None) == L.LENS_ERR_INVALID_ARG
+    assert R(None, None, None, 5, 0, 0.1, 1.0, None, 1, None) == L.LENS_ERR_INVALID_ARG
+    assert R(None, None, None, 5, 128, 0.1, 1.0, None, 1, None) == L.LENS_ERR_INVALID_ARG
+    assert R(0x1000, 0x1000, None, 5, 128, 0.1, 1.0, 0x1000, 9, None) == L.LENS_ERR_INVALID_ARG
+    assert R(None, None, None, 0, 128, 0.1, 1.0, None, 1, None) == L.LENS_OK   # empty: nothing to do
 
 
 def test_timer_argument_check():
@@ -126,3 +133,17 @@ def test_timer_argument_check():
     assert T.lens_timer_start(0b11) == L.LENS_OK
     st, ms, n = T.lens_timer_stop()
     assert st == L.LENS_OK and n == [0] * 5 and ms == [0.0] * 5
+
+
+def test_host_time_grid_matches_oracle():
+    """The sampler's host-side grid (float32) against the oracle's fp64 grid,
+    uniform and shifted."""
+    import oracle as O
+    from text_image_flow_amd import device as dv
+    for steps in (1, 4, 20, 50):
+        for mu in (None, 0.0, 1.06, -0.5):
+            g = dv.time_grid(steps, mu)
+            assert g.dtype == np.float32
+            np.testing.assert_allclose(g, O.time_grid(steps, mu), rtol=0, atol=6e-8)
+            assert g[0] == 1.0 and g[-1] == 0.0
+    assert dv.mu_for_tokens(2560, 1024, 1.06, 4096, 1.5) == O.mu_for_tokens(2560, 1024, 1.06, 4096, 1.5)

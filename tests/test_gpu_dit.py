@@ -147,8 +147,33 @@ def test_flow_step_1024(cfg_scale, use_uncond):
     assert np.array_equal(lowp.float().cpu().numpy(), synth.bf16_round(g))
 
 
+@pytest.mark.parametrize("ntok,C,cfg_scale,use_uncond", [(8192, 128, 5.0, True), (4097, 128, 1.0, True),
+                                                      (4096, 128, 5.0, False), (1001, 96, 2.5, True),
+                                                      (333, 200, 5.0, True)])
+def test_flow_step_rescaled(ntok, C, cfg_scale, use_uncond):
+    """Norm-rescaled CFG step against the oracle: 1024^2 cond+uncond latents
+    (2 x 4096 tokens of 128 channels), a ragged token count, no uncond, and
+    channel counts that are not multiples of the wave width."""
+    T, dv = _env()
+    x = synth.gaussian((ntok, C), 3, 0)
+    vc, vu = synth.gaussian((ntok, C), 3, 1), synth.gaussian((ntok, C), 3, 2)
+    # token 0: u + 5 (c - u) = 1.25 + 5 (1 - 1.25) = 0 exactly in fp32 -> unchanged
+    vc[0], vu[0] = 1.0, 1.25
+    dx = dv.upload(x)
+    lowp = torch.empty((ntok, C), dtype=torch.bfloat16, device="cuda")
+    dv.flow_step_rescaled(dx, dv.upload(vc), dv.upload(vu) if use_uncond else None, -0.05, cfg_scale, lowp)
+    torch.cuda.synchronize()
+    ref = O.flow_step_rescaled(x, vc, vu if use_uncond else None, -0.05, cfg_scale)
+    g = dx.cpu().numpy()
+    assert_parity(g, ref, f"rescaled flow step n={ntok} C={C} s={cfg_scale} uncond={use_uncond}")
+    assert np.max(np.abs(g - ref)) <= 4e-6 * np.max(np.abs(ref))
+    if use_uncond and cfg_scale == 5.0:
+        assert np.array_equal(g[0], x[0])
+    assert np.array_equal(lowp.float().cpu().numpy(), synth.bf16_round(g))
+
+
 # ------------------------------------------------------------ sampler
-def _small_sampler_setup(use_cfg):
+def _small_sampler_setup(use_cfg, **smp_kw):
     T, dv = _env()
     gh, gw, St = 8, 8, 16
     cfg = T.default_config(T.LENS_BF16)
@@ -162,7 +187,8 @@ def _small_sampler_setup(use_cfg):
     feats = np.concatenate([fc, fu]) if use_cfg else fc
     ip, tp = synth.image_positions(gh, gw), synth.text_positions(St)
     x0 = synth.latents(n, gh * gw)
-    smp = dv.Sampler(cfg, dit, dv.upload(ip), dv.upload(tp), n, gh * gw, St, 5.0 if use_cfg else 1.0, use_cfg)
+    smp = dv.Sampler(cfg, dit, dv.upload(ip), dv.upload(tp), n, gh * gw, St, 5.0 if use_cfg else 1.0, use_cfg,
+                     **smp_kw)
     return dv, top, blocks, feats, ip, tp, x0, smp
 
 
@@ -187,6 +213,28 @@ def test_sampler_cfg_teacher_forced():
         assert_parity(states[k + 1][0][0], ref, f"x_{k + 1}")
         # the increment carries the whole step; CFG 5 amplifies velocity
         # rounding by up to 5 + 4, so it gets the block-delta bar
+        assert_parity(states[k + 1][0][0] - xk[0], ref - xk[0], f"dx_{k}", rel=5e-2)
+
+
+def test_sampler_rescaled_cfg_shifted_grid_teacher_forced():
+    """Sampler with the norm-rescaled CFG step and the shifted grid (mu =
+    1.06): each step against the oracle's rescaled combine of its own dit
+    velocities at the GPU's bf16 input, on the oracle's shifted grid."""
+    dv, top, blocks, feats, ip, tp, x0, smp = _small_sampler_setup(True, mu=1.06, norm_rescale=True)
+    steps = 3
+    states = []
+    x = dv.upload(x0)
+    smp.run(x, dv.upload(synth.bf16_round(x0), 1), dv.upload(feats, 1), None, steps,
+            step_hook=lambda k, xs, xa: states.append((xs.cpu().numpy().copy(), xa.float().cpu().numpy().copy())))
+    torch.cuda.synchronize()
+    states.append((x.cpu().numpy(), None))
+    ts = O.time_grid(steps, mu=1.06)
+    for k in range(steps):
+        xk, xa = states[k]
+        t = np.array([ts[k], ts[k]])
+        v = O.dit_forward(top, blocks, xa, feats, t, ip, tp)
+        ref = O.flow_step_rescaled(xk[0], v[0], v[1], ts[k + 1] - ts[k], 5.0)
+        assert_parity(states[k + 1][0][0], ref, f"x_{k + 1}")
         assert_parity(states[k + 1][0][0] - xk[0], ref - xk[0], f"dx_{k}", rel=5e-2)
 
 

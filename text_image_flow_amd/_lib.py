@@ -19,7 +19,8 @@ KERNEL_NAMES = ("gemm", "attention", "norm", "qknorm_rope", "adaln")
 # every function lens.h declares (checked against the header by the tests)
 EXPORTS = (
     "lens_default_config", "lens_block_workspace_bytes", "lens_dit_workspace_bytes", "lens_block_forward",
-    "lens_dit_forward", "lens_flow_step", "lens_timer_start", "lens_timer_stop", "lens_status_string",
+    "lens_dit_forward", "lens_flow_step", "lens_flow_step_rescaled", "lens_timer_start", "lens_timer_stop",
+    "lens_status_string",
     "lens_last_error", "lens_version",
 )
 
@@ -76,6 +77,7 @@ def lib() -> C.CDLL:
             "lens_block_forward": (C.c_int, [cfgp, C.POINTER(LensBlockW), P, P, P, P, P, P, I32, I32, I32, P, SZ, P]),
             "lens_dit_forward": (C.c_int, [cfgp, C.POINTER(LensDitW), P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]),
             "lens_flow_step": (C.c_int, [P, P, P, I64, F, F, P, C.c_int, P]),
+            "lens_flow_step_rescaled": (C.c_int, [P, P, P, I64, I32, F, F, P, C.c_int, P]),
             "lens_timer_start": (C.c_int, [C.c_uint32]),
             "lens_timer_stop": (C.c_int, [C.POINTER(D), C.POINTER(I64)]),
             "lens_status_string": (C.c_char_p, [C.c_int]),
@@ -135,6 +137,12 @@ def lens_dit_forward(cfg, w, x, txt_feats, t, img_pos, txt_pos, txt_len, B, S_im
 
 def lens_flow_step(x, v_cond, v_uncond, n, dt, cfg_scale, x_lowp_out, lowp_dtype, stream) -> int:
     return lib().lens_flow_step(x, v_cond, v_uncond, n, dt, cfg_scale, x_lowp_out, lowp_dtype, stream)
+
+
+def lens_flow_step_rescaled(x, v_cond, v_uncond, n_tokens, channels, dt, cfg_scale, x_lowp_out, lowp_dtype,
+                            stream) -> int:
+    return lib().lens_flow_step_rescaled(x, v_cond, v_uncond, n_tokens, channels, dt, cfg_scale, x_lowp_out,
+                                         lowp_dtype, stream)
 
 
 def lens_timer_start(kind_mask: int) -> int:

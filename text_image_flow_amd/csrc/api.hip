@@ -505,6 +505,20 @@ lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond,
   return LENS_OK;
 }
 
+lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *v_uncond, int64_t n_tokens,
+                                    int32_t channels, float dt, float cfg_scale, void *x_lowp_out,
+                                    lens_dtype lowp_dtype, void *hip_stream) {
+  if (n_tokens < 0) return fail(LENS_ERR_INVALID_ARG, "n_tokens = %lld < 0", (long long)n_tokens);
+  if (channels <= 0) return fail(LENS_ERR_INVALID_ARG, "channels = %d must be positive", (int)channels);
+  if (n_tokens > 0 && (!x || !v_cond)) return fail(LENS_ERR_INVALID_ARG, "x and v_cond must not be NULL");
+  if (x_lowp_out && lowp_dtype != LENS_F32 && lowp_dtype != LENS_BF16)
+    return fail(LENS_ERR_INVALID_ARG, "lowp_dtype %d is not LENS_F32 or LENS_BF16", (int)lowp_dtype);
+  if (n_tokens > ((int64_t)1 << 40) / channels) return fail(LENS_ERR_UNSUPPORTED, "too many elements");
+  HIP_TRY(launch_flow_step_rescaled(x, v_cond, v_uncond, n_tokens, channels, dt, cfg_scale, x_lowp_out,
+                                    lowp_dtype == LENS_BF16, (hipStream_t)hip_stream));
+  return LENS_OK;
+}
+
 lens_status lens_timer_start(uint32_t mask) {
   if (mask >> LENS_KERNEL_COUNT) return fail(LENS_ERR_INVALID_ARG, "kernel mask 0x%x has unknown bits", mask);
   g_timer.mask = mask;

@@ -148,5 +148,8 @@ hipError_t launch_txt_norm(const void *feats, const void *gain, void *out, int r
 // Euler + CFG step on n elements.
 hipError_t launch_flow_step(float *x, const float *vc, const float *vu, int64_t n, float dt, float s,
                             void *lowp, int lowp_bf16, hipStream_t stream);
+// Euler + norm-rescaled CFG on ntok tokens of C channels.
+hipError_t launch_flow_step_rescaled(float *x, const float *vc, const float *vu, int64_t ntok, int C, float dt,
+                                     float s, void *lowp, int lowp_bf16, hipStream_t stream);
 
 }  // namespace lens

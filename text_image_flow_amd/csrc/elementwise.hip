@@ -507,6 +507,35 @@ __global__ void flow_step_kernel(float *x, const float *vc, const float *vu, int
   }
 }
 
+// Norm-rescaled CFG + Euler (Lens blog, "Exploring Image Editing"): one wave
+// per token of C channels; comb = u + s (c - u), rescaled by |c| / |comb|
+// (left as is where |comb| = 0), then x += dt * comb.
+template <typename TL>
+__global__ __launch_bounds__(256) void flow_step_rescaled_kernel(float *x, const float *vc, const float *vu,
+                                                                 int64_t ntok, int C, float dt, float s, TL *lowp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= ntok) return;
+  const int64_t base = tok * C;
+  float nc = 0.f, nb = 0.f;
+  for (int ch = lane; ch < C; ch += 64) {
+    const float c = vc[base + ch];
+    const float v = vu ? vu[base + ch] + s * (c - vu[base + ch]) : c;
+    nc = fmaf(c, c, nc);
+    nb = fmaf(v, v, nb);
+  }
+  nc = wave_sum(nc);
+  nb = wave_sum(nb);
+  const float f = nb > 0.f ? sqrtf(nc) / sqrtf(nb) : 1.f;
+  for (int ch = lane; ch < C; ch += 64) {
+    const float c = vc[base + ch];
+    const float v = vu ? vu[base + ch] + s * (c - vu[base + ch]) : c;
+    const float xn = x[base + ch] + dt * (v * f);
+    x[base + ch] = xn;
+    if (lowp) lowp[base + ch] = from_f32<TL>(xn);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float eps, bool bf16_path,
@@ -636,6 +665,20 @@ hipError_t launch_flow_step(float *x, const float *vc, const float *vu, int64_t 
   else
     hipLaunchKernelGGL(flow_step_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, x, vc, vu, n, dt, s,
                        (float *)lowp);
+  return hipGetLastError();
+}
+
+hipError_t launch_flow_step_rescaled(float *x, const float *vc, const float *vu, int64_t ntok, int C, float dt,
+                                     float s, void *lowp, int lowp_bf16, hipStream_t stream) {
+  if (ntok <= 0) return hipSuccess;
+  const int64_t blocks = (ntok + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (lowp && lowp_bf16)
+    hipLaunchKernelGGL(flow_step_rescaled_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, vc, vu, ntok,
+                       C, dt, s, (bf16 *)lowp);
+  else
+    hipLaunchKernelGGL(flow_step_rescaled_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, x, vc, vu,
+                       ntok, C, dt, s, (float *)lowp);
   return hipGetLastError();
 }
 

@@ -125,9 +125,29 @@ def flow_step(x, v_cond, v_uncond, dt, cfg_scale, x_lowp=None, lowp_dtype=L.LENS
                              ptr(x_lowp), lowp_dtype, stream_handle(stream)))
 
 
-def time_grid(steps: int) -> np.ndarray:
-    """t_k = 1 - k/N, k = 0..N (noise at t = 1), as float32."""
-    return (1.0 - np.arange(steps + 1, dtype=np.float64) / steps).astype(np.float32)
+def flow_step_rescaled(x, v_cond, v_uncond, dt, cfg_scale, x_lowp=None, lowp_dtype=L.LENS_BF16, stream=None):
+    """Norm-rescaled CFG Euler step over the tokens of x (channels = last dim)."""
+    C = int(x.shape[-1])
+    L.check(L.lens_flow_step_rescaled(ptr(x), ptr(v_cond), ptr(v_uncond), x.numel() // C, C, float(dt),
+                                      float(cfg_scale), ptr(x_lowp), lowp_dtype, stream_handle(stream)))
+
+
+def time_grid(steps: int, mu: float | None = None) -> np.ndarray:
+    """t_k = 1 - k/N, k = 0..N (noise at t = 1), as float32.  With mu, each
+    point moves to e^mu t / (e^mu t + 1 - t) (a shift by mu in logit space,
+    end points fixed): the resolution-dependent schedule of the Lens paper
+    summary (前置知识 and 方法步骤详情: mu(n) linear in the token count,
+    mu = 1.06 at 512^2)."""
+    t = 1.0 - np.arange(steps + 1, dtype=np.float64) / steps
+    if mu is not None:
+        e = float(np.exp(mu))
+        t = e * t / (e * t + 1.0 - t)
+    return t.astype(np.float32)
+
+
+def mu_for_tokens(n: int, n0: float, mu0: float, n1: float, mu1: float) -> float:
+    """mu on the line through (n0, mu0) and (n1, mu1), at token count n."""
+    return mu0 + (float(n) - n0) * (mu1 - mu0) / (n1 - n0)
 
 
 class Sampler:
@@ -139,7 +159,10 @@ class Sampler:
     the host inside the loop."""
 
     def __init__(self, cfg, dit: DeviceDit, img_pos, txt_pos, n: int, S_img: int, S_txt: int, cfg_scale: float,
-                 use_cfg: bool, device="cuda"):
+                 use_cfg: bool, device="cuda", mu: float | None = None, norm_rescale: bool = False):
+        """mu: timestep shift of the grid (None: uniform grid); norm_rescale:
+        norm-rescaled CFG (lens_flow_step_rescaled) instead of the plain one."""
+        self.mu, self.norm_rescale = mu, bool(norm_rescale)
         self.cfg, self.dit = cfg, dit
         self.img_pos, self.txt_pos = img_pos, txt_pos
         self.n, self.S_img, self.S_txt = n, S_img, S_txt
@@ -156,7 +179,7 @@ class Sampler:
         """x: [n, S_img, in_ch] float32 latent tokens, updated in place;
         x_act0: the same values in the activation type (the first DiT input).
         txt_feats: [B, S_txt, F] act type (cond rows first); txt_len [B] or None."""
-        ts = time_grid(steps)
+        ts = time_grid(steps, self.mu)
         t_tab = upload(np.repeat(ts[:, None], self.B, axis=1), None, self.device)   # [steps+1, B]
         # first input, duplicated for the uncond half (plain copies)
         for h in range(self.B // self.n):
@@ -168,7 +191,8 @@ class Sampler:
                         self.v, self.ws)
             vc = self.v[:self.n]
             vu = self.v[self.n:] if self.use_cfg else None
-            flow_step(x, vc, vu, float(ts[k + 1] - ts[k]), self.cfg_scale, self.x_act[:self.n], self.cfg.act_dtype)
+            step = flow_step_rescaled if self.norm_rescale else flow_step
+            step(x, vc, vu, float(ts[k + 1] - ts[k]), self.cfg_scale, self.x_act[:self.n], self.cfg.act_dtype)
             if self.use_cfg:
                 self.x_act[self.n:].copy_(self.x_act[:self.n])
         return x
