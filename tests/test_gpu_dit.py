@@ -63,6 +63,26 @@ def test_dit_two_blocks_bf16_masked():
     check_dit(2, "bf16", 2, 8, 10, 24, txt_len=[24, 9])
 
 
+@pytest.mark.parametrize("order", [[2, 0, 2], [1], [2, 1, 0]])
+def test_dit_block_list(order):
+    """Block removal / swap / repeat: the model built with blocks 0..2 run as
+    the block sequence `order` against the oracle on that sequence."""
+    T, dv = _env()
+    print(f"dit block list {order}", flush=True)
+    x, feats, t, ip, tp = make_inputs(2, 8, 10, 24, "bf16", [24, 9])
+    top = synth.top_weights(dtype="bf16")
+    blocks = [synth.block_weights(i, dtype="bf16") for i in range(3)]
+    dit = dv.DeviceDit(top, blocks, T.LENS_BF16).with_blocks(order)
+    cfg = T.default_config(T.LENS_BF16)
+    cfg.n_blocks = len(order)
+    v = torch.empty((2, 80, cfg.out_ch), dtype=torch.float32, device="cuda")
+    dv.dit_forward(cfg, dit, dv.upload(x, T.LENS_BF16), dv.upload(feats, T.LENS_BF16), dv.upload(t), dv.upload(ip),
+                   dv.upload(tp), dv.upload(np.array([24, 9], np.int32)), v, dv.Workspace())
+    torch.cuda.synchronize()
+    ref = O.dit_forward(top, [blocks[i] for i in order], x, feats, t, ip, tp, [24, 9])
+    assert_parity(v.cpu().numpy(), ref, f"v (blocks {order})")
+
+
 def test_dit_two_blocks_f32():
     check_dit(2, "f32", 1, 7, 9, 16)
 

@@ -69,6 +69,19 @@ class DeviceDit:
     def __init__(self, top: dict, blocks, act_dtype: int, device="cuda"):
         self.top = {k: upload(v, act_dtype, device) if v is not None else None for k, v in top.items()}
         self.blocks = [b if isinstance(b, DeviceBlock) else DeviceBlock(b, act_dtype, device) for b in blocks]
+        self._tables()
+
+    def with_blocks(self, order):
+        """The same weights run as the block sequence `order` (indices into
+        this model's blocks; repeats and omissions allowed): block swap and
+        block removal without copying weights.  Set cfg.n_blocks = len(order)."""
+        view = object.__new__(DeviceDit)
+        view.top = self.top
+        view.blocks = [self.blocks[i] for i in order]
+        view._tables()
+        return view
+
+    def _tables(self):
         self.block_array = (L.LensBlockW * max(1, len(self.blocks)))()
         for i, b in enumerate(self.blocks):
             self.block_array[i] = b.table
