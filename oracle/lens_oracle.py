@@ -148,13 +148,21 @@ def swiglu_mlp(a, w1, b1, w3, b3, w2, b2):
 # one double-stream block
 # --------------------------------------------------------------------------
 
-def _stream_qkv(ws, a, heads, eps):
+def _proj(x, w, b, fp8):
+    """A block projection; with fp8, both operands as the MX fp8 GEMM sees
+    them (mx_roundtrip along the reduction axis)."""
+    if fp8:
+        return linear(mx_roundtrip(x), mx_roundtrip(w), b)
+    return linear(x, w, b)
+
+
+def _stream_qkv(ws, a, heads, eps, fp8=False):
     """QKV projection, then per-head RMSNorm of q and k with the stream's
     64-d gains ([turbo] norm_q/norm_k for the image stream,
     norm_added_q/norm_added_k for the text stream).  READING: output columns
     are q | k | v, each heads x head_dim; the norm comes before RoPE."""
     B, S, D = a.shape
-    qkv = linear(a, ws["qkv_w"], ws.get("qkv_b"))
+    qkv = _proj(a, ws["qkv_w"], ws.get("qkv_b"), fp8)
     q, k, v = (qkv[..., i * D:(i + 1) * D].reshape(B, S, heads, D // heads) for i in range(3))
     q = rms_norm(q, eps, ws["q_gain"])
     k = rms_norm(k, eps, ws["k_gain"])
@@ -162,7 +170,7 @@ def _stream_qkv(ws, a, heads, eps):
 
 
 def block_forward(w, h_img, h_txt, temb, img_pos, txt_pos, txt_len=None, *,
-                  heads=24, axes=(8, 28, 28), theta=10000.0, eps=1e-6, rows=None):
+                  heads=24, axes=(8, 28, 28), theta=10000.0, eps=1e-6, rows=None, gemm_fp8=False):
     """One double-stream MM-DiT block ([paper] 前置知识, MMDiT: each stream
     runs its own RMSNorm-attention-MLP branch and the two meet in joint
     attention; [turbo] "双流注意力机制", "自适应调制与 RMSNorm").
@@ -175,6 +183,9 @@ def block_forward(w, h_img, h_txt, temb, img_pos, txt_pos, txt_len=None, *,
     rows are carried through attention, the projections and the MLP (keys
     and values still come from every token), and the result is
     (h_img[:, img_rows], h_txt[:, txt_rows]) of the full block.
+
+    gemm_fp8: the qkv, out, w1, w3 and w2 projections take MX fp8 operands
+    (the low-precision variant above); everything else is unchanged.
 
     Text keys j >= txt_len[b] are masked ([blog] "Exploring Text Encoder":
     the DiT never sees the zero padding).  Rows of padded text queries are
@@ -200,7 +211,7 @@ def block_forward(w, h_img, h_txt, temb, img_pos, txt_pos, txt_len=None, *,
     qkv = {}
     for s in ("img", "txt"):
         a = modulate(rms_norm(h[s], eps), mod[s]["shift1"], mod[s]["scale1"])
-        q, k, v = _stream_qkv(w[s], a, heads, eps)
+        q, k, v = _stream_qkv(w[s], a, heads, eps, gemm_fp8)
         q = np.stack([rope(q[b], pos[s], axes, theta) for b in range(B)])
         k = np.stack([rope(k[b], pos[s], axes, theta) for b in range(B)])
         qkv[s] = (q, k, v)
@@ -216,14 +227,18 @@ def block_forward(w, h_img, h_txt, temb, img_pos, txt_pos, txt_len=None, *,
         nt = len(sel["txt"])
         O_s = {"txt": O[:nt], "img": O[nt:]}
         for s in ("img", "txt"):
-            y = linear(O_s[s], w[s]["out_w"], w[s].get("out_b"))
+            y = _proj(O_s[s], w[s]["out_w"], w[s].get("out_b"), gemm_fp8)
             out[s][b] = out[s][b] + mod[s]["gate1"][b] * y
 
     # pre-MLP RMSNorm + modulation, gated SwiGLU MLP
     for s in ("img", "txt"):
         a = modulate(rms_norm(out[s], eps), mod[s]["shift2"], mod[s]["scale2"])
-        y = swiglu_mlp(a, w[s]["w1_w"], w[s].get("w1_b"), w[s]["w3_w"], w[s].get("w3_b"),
-                       w[s]["w2_w"], w[s].get("w2_b"))
+        if gemm_fp8:
+            u = silu(_proj(a, w[s]["w1_w"], w[s].get("w1_b"), True)) * _proj(a, w[s]["w3_w"], w[s].get("w3_b"), True)
+            y = _proj(u, w[s]["w2_w"], w[s].get("w2_b"), True)
+        else:
+            y = swiglu_mlp(a, w[s]["w1_w"], w[s].get("w1_b"), w[s]["w3_w"], w[s].get("w3_b"),
+                           w[s]["w2_w"], w[s].get("w2_b"))
         out[s] = out[s] + mod[s]["gate2"][:, None, :] * y
     return out["img"], out["txt"]
 
@@ -274,7 +289,7 @@ def final_layer(top, h_img, temb, *, eps=1e-6):
 
 def dit_forward(top, blocks, x, txt_feats, t, img_pos, txt_pos, txt_len=None, *,
                 heads=24, axes=(8, 28, 28), theta=10000.0, eps=1e-6, t_freq=256,
-                t_scale=1000.0, txt_layers=4, capture=None):
+                t_scale=1000.0, txt_layers=4, capture=None, gemm_fp8=False):
     """Whole denoiser: v = proj_out(norm_out(blocks(img_in(x), txt_in(f)))).
     blocks: iterable of block weight dicts (generated lazily by the caller).
     x [B, Si, in_ch] patchified tokens (a 2x2 patch of the 32-channel latent
@@ -285,7 +300,7 @@ def dit_forward(top, blocks, x, txt_feats, t, img_pos, txt_pos, txt_len=None, *,
     h_txt = text_embed(top, txt_feats, layers=txt_layers, eps=eps)
     for i, wb in enumerate(blocks):
         h_img, h_txt = block_forward(wb, h_img, h_txt, temb, img_pos, txt_pos, txt_len,
-                                     heads=heads, axes=axes, theta=theta, eps=eps)
+                                     heads=heads, axes=axes, theta=theta, eps=eps, gemm_fp8=gemm_fp8)
         if capture is not None:
             capture[i] = (h_img, h_txt)
     return final_layer(top, h_img, temb, eps=eps)
@@ -375,6 +390,69 @@ def sample(velocity, x0, steps, scale=1.0, use_uncond=False):
     return x
 
 
+# --------------------------------------------------------------------------
+# low-precision GEMM variant (MX fp8)
+# --------------------------------------------------------------------------
+# [4bit] section 4: the DiT's projection weights are quantized (int4, groups
+# of 64) while img_in, txt_in, proj_out, the timestep/text embedders and
+# norm_out stay bf16; a single DiT pass keeps cosine 0.9976 against the
+# reference.  READING (MI355X analogue): the per-block projections (qkv, out,
+# w1, w3, w2) take MX fp8 operands -- e4m3 elements with one power-of-two
+# scale per 32 consecutive elements along the reduction axis -- for both the
+# weights and the activations entering them; AdaLN and everything outside
+# the blocks stay as they are.
+
+E4M3_MAX = 448.0     # largest finite e4m3 value (1.75 * 2^8)
+E4M3_MIN_NORMAL = 2.0 ** -6
+E4M3_SUB_STEP = 2.0 ** -9
+
+
+def round_e4m3(y):
+    """Round to the nearest e4m3 value (ties to even), for |y| <= 448: 3
+    mantissa bits on normals (exponents -6..8), steps of 2^-9 below 2^-6."""
+    y = _f(y)
+    a = np.abs(y)
+    e = np.floor(np.log2(np.where(a >= E4M3_MIN_NORMAL, a, 1.0)))
+    step = np.where(a >= E4M3_MIN_NORMAL, 2.0 ** (e - 3), E4M3_SUB_STEP)
+    q = np.round(a / step) * step          # np.round: ties to even
+    return np.sign(y) * q
+
+
+def mx_scale_exponent(amax):
+    """Smallest integer e with amax <= 448 * 2^e (amax > 0), clamped to the
+    E8M0 range [-127, 127]; -127 for amax = 0.  READING: the scale is chosen
+    so that no element saturates."""
+    amax = _f(amax)
+    e = np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX))
+    # log2 of an exact power-of-two ratio can land a hair off an integer
+    e = np.where(amax > E4M3_MAX * 2.0 ** e, e + 1, e)
+    e = np.where(amax <= E4M3_MAX * 2.0 ** (e - 1), e - 1, e)
+    return np.clip(np.where(amax > 0, e, -127), -127, 127).astype(np.int64)
+
+
+def mx_quantize(x, block=32):
+    """MX fp8 along the last axis: per block of 32, e = mx_scale_exponent of
+    the block's max |x|, elements round_e4m3(x / 2^e).  Returns (q, e) with q
+    on the e4m3 grid and e of shape [..., n / 32]."""
+    x = _f(x)
+    n = x.shape[-1]
+    xb = x.reshape(x.shape[:-1] + (n // block, block))
+    e = mx_scale_exponent(np.max(np.abs(xb), axis=-1))
+    q = round_e4m3(xb / 2.0 ** e[..., None])
+    return q.reshape(x.shape), e
+
+
+def mx_dequantize(q, e, block=32):
+    q = _f(q)
+    n = q.shape[-1]
+    return (q.reshape(q.shape[:-1] + (n // block, block)) * 2.0 ** _f(e)[..., None]).reshape(q.shape)
+
+
+def mx_roundtrip(x, block=32):
+    """The value an MX fp8 GEMM sees for x: dequantize(quantize(x))."""
+    return mx_dequantize(*mx_quantize(x, block), block)
+
+
 def stream_param_count(shapes):
     """Weights of one stream (biases and 64-d gains excluded), from the shape
     table of the tensors the block above reads."""
@@ -386,4 +464,5 @@ __all__ = [
     "swiglu_mlp", "block_forward", "timestep_features", "timestep_embedding", "text_embed",
     "final_layer", "dit_forward", "time_grid", "cfg_combine", "euler_step", "flow_step",
     "cfg_combine_rescaled", "flow_step_rescaled", "time_shift", "mu_for_tokens", "sample", "stream_param_count",
+    "E4M3_MAX", "round_e4m3", "mx_scale_exponent", "mx_quantize", "mx_dequantize", "mx_roundtrip",
 ]

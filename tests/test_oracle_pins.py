@@ -550,3 +550,92 @@ def test_shifted_grid_and_mu_line():
     assert O.mu_for_tokens(1024, 1024, 1.06, 4096, 1.5) == 1.06
     assert abs(O.mu_for_tokens(4096, 1024, 1.06, 4096, 1.5) - 1.5) < 1e-15
     assert abs(O.mu_for_tokens(2560, 1024, 1.06, 4096, 1.5) - 1.28) < 1e-12
+
+
+# ------------------------------------------------------------ MX fp8 (e4m3)
+def _e4m3_decode(code):
+    """OCP e4m3 (fn) decode from its bit fields: sign, 4-bit exponent with
+    bias 7, 3-bit mantissa; exponent 0 is subnormal; 0x7f / 0xff are NaN."""
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 0:
+        return s * m / 8.0 * 2.0 ** -6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def test_e4m3_grid_is_fixed_and_ties_go_to_even():
+    pos = np.array([_e4m3_decode(c) for c in range(1, 0x7F)])          # all positive finite codes
+    assert len(set(pos)) == 126 and pos.max() == 448.0 and pos.min() == 2.0 ** -9
+    assert np.all(np.diff(pos) > 0)
+    grid = np.concatenate([-pos[::-1], [0.0], pos])
+    np.testing.assert_array_equal(O.round_e4m3(grid), grid)
+    # midpoints go to the neighbour whose code is even (mantissa LSB 0)
+    codes = np.arange(1, 0x7E)
+    mid = 0.5 * (pos[:-1] + pos[1:])
+    want = np.where(codes % 2 == 0, pos[:-1], pos[1:])
+    np.testing.assert_array_equal(O.round_e4m3(mid), want)
+    np.testing.assert_array_equal(O.round_e4m3(-mid), -want)
+    # just off the midpoints: the nearer neighbour
+    np.testing.assert_array_equal(O.round_e4m3(mid * (1 - 1e-9)), pos[:-1])
+    np.testing.assert_array_equal(O.round_e4m3(mid * (1 + 1e-9)), pos[1:])
+    assert O.round_e4m3(2.0 ** -10) == 0.0 and O.round_e4m3(2.0 ** -10 * 1.0001) == 2.0 ** -9
+
+
+def test_mx_scale_exponent_closed_form():
+    for k in (-100, -9, -1, 0, 1, 7, 100):
+        assert O.mx_scale_exponent(448.0 * 2.0 ** k) == k
+        assert O.mx_scale_exponent(448.0 * 2.0 ** k * (1 + 2e-16 * 8)) == k + 1
+        assert O.mx_scale_exponent(448.0 * 2.0 ** (k - 1) * (1 + 1e-12)) == k
+    assert O.mx_scale_exponent(0.0) == -127
+    assert O.mx_scale_exponent(1e-60) == -127 and O.mx_scale_exponent(1e60) == 127
+
+
+def test_mx_quantize_bounds_and_idempotence():
+    rs = np.random.default_rng(5)
+    x = rs.standard_normal((6, 128)) * np.exp(rs.uniform(-8, 8, (6, 1)))
+    x[0, :32] = 0.0                                       # an all-zero block
+    x[1, 5] = 1e4                                         # an outlier block
+    q, e = O.mx_quantize(x)
+    assert e.shape == (6, 4) and e[0, 0] == -127 and np.all(q[0, :32] == 0)
+    np.testing.assert_array_equal(O.round_e4m3(q), q)                 # on the grid
+    assert np.all(np.abs(q) <= 448.0)
+    blockmax = np.abs(x).reshape(6, 4, 32).max(-1) / 2.0 ** e
+    assert np.all(((blockmax > 224.0) & (blockmax <= 448.0)) | (e == -127))   # the tightest scale
+    dq = O.mx_dequantize(q, e)
+    # error: half a step of the element's binade (relative 2^-4), or half a
+    # subnormal step
+    scale = 2.0 ** np.repeat(e, 32, axis=1)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 0.5 * 2.0 ** -9 * scale)
+    assert np.all(np.abs(dq - x) <= bound * (1 + 1e-12))
+    np.testing.assert_array_equal(O.mx_roundtrip(dq), dq)            # idempotent
+
+
+def test_block_fp8_variant_reduces_to_quantized_operands():
+    """With gemm_fp8 the block equals the plain block run on weights and
+    activations that are already MX-quantized where the projections read
+    them: quantizing the weights beforehand changes nothing (the roundtrip
+    is idempotent), and the output stays close to the exact block."""
+    rs = np.random.default_rng(7)
+    D, H, F = 128, 2, 256
+    def stream(seed):
+        g = np.random.default_rng(seed)
+        n = lambda *s: g.standard_normal(s) * 0.05
+        return {"mod_w": n(6 * D, D), "mod_b": n(6 * D), "qkv_w": n(3 * D, D), "qkv_b": n(3 * D),
+                "out_w": n(D, D), "out_b": n(D), "w1_w": n(F, D), "w1_b": n(F), "w3_w": n(F, D), "w3_b": n(F),
+                "w2_w": n(D, F), "w2_b": n(D), "q_gain": 1 + n(64), "k_gain": 1 + n(64)}
+    w = {"img": stream(1), "txt": stream(2)}
+    hi, ht, temb = rs.standard_normal((1, 12, D)), rs.standard_normal((1, 5, D)), rs.standard_normal((1, D))
+    ip = np.stack([np.zeros(12, int), np.arange(12) // 4, np.arange(12) % 4], 1)
+    tp = np.zeros((5, 3), int)
+    kw = dict(heads=H, axes=(8, 28, 28))
+    a8 = O.block_forward(w, hi, ht, temb, ip, tp, gemm_fp8=True, **kw)
+    wq = {s: {k: (O.mx_roundtrip(v) if k in ("qkv_w", "out_w", "w1_w", "w3_w", "w2_w") else v)
+              for k, v in w[s].items()} for s in w}
+    b8 = O.block_forward(wq, hi, ht, temb, ip, tp, gemm_fp8=True, **kw)
+    for x, y in zip(a8, b8):
+        np.testing.assert_array_equal(x, y)
+    ex = O.block_forward(w, hi, ht, temb, ip, tp, **kw)
+    for x, y, h in zip(a8, ex, (hi, ht)):
+        dx, dy = (x - h).ravel(), (y - h).ravel()
+        assert dx @ dy / np.linalg.norm(dx) / np.linalg.norm(dy) > 0.998     # block update direction kept
+        assert not np.array_equal(x, y)                                        # and it is a different path
