@@ -6,8 +6,8 @@ one MI355X.
 A step is the whole hot path: lens_dit_forward on a batch of 2 (cond and
 uncond samples sharing x and t: timestep MLP, AdaLN of all blocks, img_in,
 txt_norm + txt_in, 48 double-stream blocks, norm_out + proj_out) followed by
-lens_flow_step (CFG 5.0 combine + Euler update + bf16 copy of x for the next
-forward).  Weights are random-init bf16 (N(0, 0.02)), inputs are seeded
+lens_flow_step_rescaled (Lens's norm-rescaled CFG at scale 5.0 + Euler
+update + bf16 copy of x for the next forward).  Weights are random-init bf16 (N(0, 0.02)), inputs are seeded
 synthetic tensors of the real shapes, and everything is resident in HBM
 before the timed region starts.
 
@@ -17,6 +17,10 @@ valid keys).  A second timed region records HIP events around every kernel
 launch (the library's opt-in timer) for the per-family breakdown and the
 roofline of the dominant kernel family.  `cpu_baseline` times the fp64
 oracle on a bounded sample (one block at the same shape) on the host cores.
+`fp8_variant` times the same step with the block projections as MX fp8
+GEMMs (weights quantized on the device from the same bf16 weights) and
+reports the cosine of its velocity against the bf16 step's on one input;
+`value` is always the bf16 step.
 """
 from __future__ import annotations
 
@@ -113,6 +117,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timer", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the MX fp8 variant")
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (counter calibration) and exit")
     args = ap.parse_args()
@@ -164,12 +169,13 @@ def main():
     setup_s = time.perf_counter() - t_setup
 
     k_state = [0]
+    model = [cfg, dit]
 
     def step():
         k = k_state[0] % LOOP_STEPS
         k_state[0] += 1
-        dv.dit_forward(cfg, dit, x_act, feats, t_tab[k], ip, tp, None, v, ws)
-        dv.flow_step(x, v[:1], v[1:], float(ts[k + 1] - ts[k]), CFG_SCALE, x_act[:1], T.LENS_BF16)
+        dv.dit_forward(model[0], model[1], x_act, feats, t_tab[k], ip, tp, None, v, ws)
+        dv.flow_step_rescaled(x, v[:1], v[1:], float(ts[k + 1] - ts[k]), CFG_SCALE, x_act[:1], T.LENS_BF16)
         x_act[1:].copy_(x_act[:1])
 
     for _ in range(args.warmup):
@@ -222,6 +228,47 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flops_per_launch": per_launch_flops, "avg_launch_us": round(avg_s * 1e6, 2)}
 
+    # ---- MX fp8 variant of the same step (not the headline value)
+    fp8 = None
+    if not args.no_fp8:
+        cfg8 = T.default_config(T.LENS_BF16)
+        cfg8.gemm_fp8 = 1
+        dit8 = dv.DeviceDit(top, [dv.DeviceBlock.fp8_copy(b) for b in blocks], T.LENS_BF16)
+        ws.get(T.lens_dit_workspace_bytes(cfg8, B, S_IMG, S_TXT))
+        # velocity of both variants on the current input
+        va = torch.empty_like(v)
+        dv.dit_forward(cfg, dit, x_act, feats, t_tab[0], ip, tp, None, va, ws)
+        dv.dit_forward(cfg8, dit8, x_act, feats, t_tab[0], ip, tp, None, v, ws)
+        torch.cuda.synchronize()
+        a, b8 = va.double().flatten(), v.double().flatten()
+        cosv = float((a @ b8) / (a.norm() * b8.norm()))
+        model[:] = [cfg8, dit8]
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms8 = e0.elapsed_time(e1) / args.steps
+        fk = {}
+        if not args.no_kernel_timer:
+            L.check(T.lens_timer_start((1 << L.LENS_KERNEL_COUNT) - 1))
+            for _ in range(args.steps):
+                step()
+            torch.cuda.synchronize()
+            st8, ms_k, n_k = T.lens_timer_stop()
+            L.check(st8)
+            for i, name in enumerate(L.KERNEL_NAMES):
+                if n_k[i]:
+                    fk[name] = {"ms_per_step": round(ms_k[i] / args.steps, 4)}
+        model[:] = [cfg, dit]
+        fp8 = {"ms_per_step": round(ms8, 3), "TFLOP/s": round(fl["total"] / (ms8 * 1e-3) / 1e12, 2),
+               "speedup_vs_bf16": round(ms_step / ms8, 3), "v_cosine_vs_bf16": round(cosv, 6),
+               "format": "MX fp8: e4m3 elements, E8M0 scale per 32 along K, weights and activations of the "
+                         "block projections (qkv, out, w1, w3, w2)", "kernels": fk}
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(d)
 
     out = {
@@ -230,12 +277,12 @@ def main():
         "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Lens MM-DiT CFG denoising step, 1024x1024", "image_tokens": S_IMG,
-                   "text_tokens": S_TXT, "batch": B, "cfg": "cond+uncond in one batch, scale 5.0",
+                   "text_tokens": S_TXT, "batch": B, "cfg": "cond+uncond in one batch, norm-rescaled, scale 5.0",
                    "blocks": d.n_blocks, "hidden": d.hidden, "heads": d.heads, "mlp": d.mlp,
                    "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": fl["total"], "wall_s": round(wall, 3), "setup_s": round(setup_s, 1),
-        "kernels": kernels, "roofline": roof, "cpu_baseline": cpu,
+        "kernels": kernels, "roofline": roof, "cpu_baseline": cpu, "fp8_variant": fp8,
     }
     print(json.dumps(out))
 

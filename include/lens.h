@@ -77,12 +77,20 @@ typedef struct {
   float eps;            /* 1e-6, all RMSNorms */
   float t_scale;        /* 1000: the sinusoid sees t_scale * t */
   lens_dtype act_dtype; /* element type of weights and activations */
+  int32_t gemm_fp8;     /* 1: the block projections qkv, out, w1, w3, w2 run as
+                           MX fp8 GEMMs (requires act_dtype LENS_BF16; see
+                           lens_quantize_mxfp8); 0 (default): act_dtype */
 } lens_config;
 
-/* One Linear layer: w [out, in] in act_dtype, b [out] in act_dtype or NULL. */
+/* One Linear layer: w [out, in] in act_dtype, b [out] in act_dtype or NULL.
+ * With cfg->gemm_fp8, the qkv, out, w1, w3 and w2 layers of every block
+ * instead hold w as MX fp8: e4m3 bytes [out, in] with w_scale its E8M0
+ * scales [out, in / 32] (lens_quantize_mxfp8 of the act_dtype weight); b
+ * stays in act_dtype.  w_scale is ignored otherwise. */
 typedef struct {
   const void *w;
   const void *b;
+  const void *w_scale;
 } lens_linear;
 
 /* Weights of one stream of one block.  q_gain / k_gain: [head_dim] gains of
@@ -193,6 +201,23 @@ lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *
                                     lens_dtype lowp_dtype, void *hip_stream);
 
 /*
+ * MX fp8 quantization of a row-major matrix along its rows: src [rows, cols]
+ * (src_dtype LENS_BF16 or LENS_F32, cols a positive multiple of 32) ->
+ * q_out [rows, cols] e4m3 bytes and scale_out [rows, cols / 32] E8M0 bytes
+ * (value = 2^(byte - 127)).  Per block of 32 consecutive elements the scale
+ * is the smallest power of two 2^e with max|x| <= 448 2^e (e clamped to
+ * [-127, 127]; an all-zero block gets e = -127), and each element is
+ * x / 2^e rounded to the nearest e4m3 value, ties to even.  This is the
+ * weight format of cfg->gemm_fp8 (the low-precision DiT variant of the
+ * Lens-3.8B-4bit pipeline article (2kiu.com), section 4: projection weights
+ * quantized, img_in, txt_in, proj_out, the embedders and norm_out kept in
+ * bf16; here as MX fp8 rather than int4, the format the MI355X matrix cores
+ * take directly).  Device pointers; rows >= 0.
+ */
+lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t rows, int32_t cols, void *q_out,
+                                void *scale_out, void *hip_stream);
+
+/*
  * Opt-in kernel timer for measurement.  lens_timer_start(mask) makes every
  * later launch of the kernel families whose bit (1 << lens_kernel_kind) is
  * set record a pair of HIP events around itself, on the stream it is
@@ -205,7 +230,7 @@ lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *
 typedef enum {
   LENS_KERNEL_GEMM = 0,        /* bf16 MFMA GEMM (all projections) */
   LENS_KERNEL_ATTENTION = 1,   /* joint flash attention */
-  LENS_KERNEL_NORM = 2,        /* RMSNorm + modulation */
+  LENS_KERNEL_NORM = 2,        /* RMSNorm + modulation; MX fp8 activation quantization */
   LENS_KERNEL_QKNORM_ROPE = 3, /* QK RMSNorm + RoPE + joint layout */
   LENS_KERNEL_ADALN = 4,       /* skinny GEMV (AdaLN, timestep MLP) */
   LENS_KERNEL_COUNT = 5

@@ -147,3 +147,21 @@ def test_host_time_grid_matches_oracle():
             np.testing.assert_allclose(g, O.time_grid(steps, mu), rtol=0, atol=6e-8)
             assert g[0] == 1.0 and g[-1] == 0.0
     assert dv.mu_for_tokens(2560, 1024, 1.06, 4096, 1.5) == O.mu_for_tokens(2560, 1024, 1.06, 4096, 1.5)
+
+
+def test_fp8_argument_checks():
+    Q = T.lens_quantize_mxfp8
+    assert Q(None, 1, -1, 64, None, None, None) == L.LENS_ERR_INVALID_ARG
+    assert Q(None, 1, 4, 48, None, None, None) == L.LENS_ERR_INVALID_ARG      # cols not a multiple of 32
+    assert Q(None, 7, 4, 64, None, None, None) == L.LENS_ERR_INVALID_ARG      # bad dtype
+    assert Q(None, 1, 4, 64, None, None, None) == L.LENS_ERR_INVALID_ARG      # NULL pointers
+    assert Q(None, 1, 0, 64, None, None, None) == L.LENS_OK                   # empty: nothing to do
+    cfg = T.default_config(L.LENS_F32)
+    assert cfg.gemm_fp8 == 0
+    cfg.gemm_fp8 = 1                                                          # needs bf16 activations
+    assert T.lens_block_workspace_bytes(cfg, 1, 16, 8) == 0
+    cfg = T.default_config(L.LENS_BF16)
+    cfg.gemm_fp8 = 2
+    assert T.lens_block_workspace_bytes(cfg, 1, 16, 8) == 0
+    cfg.gemm_fp8 = 1
+    assert T.lens_block_workspace_bytes(cfg, 1, 16, 8) > T.lens_block_workspace_bytes(T.default_config(L.LENS_BF16), 1, 16, 8)

@@ -19,7 +19,8 @@ KERNEL_NAMES = ("gemm", "attention", "norm", "qknorm_rope", "adaln")
 # every function lens.h declares (checked against the header by the tests)
 EXPORTS = (
     "lens_default_config", "lens_block_workspace_bytes", "lens_dit_workspace_bytes", "lens_block_forward",
-    "lens_dit_forward", "lens_flow_step", "lens_flow_step_rescaled", "lens_timer_start", "lens_timer_stop",
+    "lens_dit_forward", "lens_flow_step", "lens_flow_step_rescaled", "lens_quantize_mxfp8", "lens_timer_start",
+    "lens_timer_stop",
     "lens_status_string",
     "lens_last_error", "lens_version",
 )
@@ -31,11 +32,12 @@ class LensConfig(C.Structure):
         ("n_blocks", C.c_int32), ("rope_axes", C.c_int32 * 3), ("in_ch", C.c_int32), ("out_ch", C.c_int32),
         ("txt_feat_dim", C.c_int32), ("txt_layers", C.c_int32), ("t_freq_dim", C.c_int32),
         ("rope_theta", C.c_float), ("eps", C.c_float), ("t_scale", C.c_float), ("act_dtype", C.c_int),
+        ("gemm_fp8", C.c_int32),
     ]
 
 
 class LensLinear(C.Structure):
-    _fields_ = [("w", C.c_void_p), ("b", C.c_void_p)]
+    _fields_ = [("w", C.c_void_p), ("b", C.c_void_p), ("w_scale", C.c_void_p)]
 
 
 class LensStreamW(C.Structure):
@@ -78,6 +80,7 @@ def lib() -> C.CDLL:
             "lens_dit_forward": (C.c_int, [cfgp, C.POINTER(LensDitW), P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]),
             "lens_flow_step": (C.c_int, [P, P, P, I64, F, F, P, C.c_int, P]),
             "lens_flow_step_rescaled": (C.c_int, [P, P, P, I64, I32, F, F, P, C.c_int, P]),
+            "lens_quantize_mxfp8": (C.c_int, [P, C.c_int, I64, I32, P, P, P]),
             "lens_timer_start": (C.c_int, [C.c_uint32]),
             "lens_timer_stop": (C.c_int, [C.POINTER(D), C.POINTER(I64)]),
             "lens_status_string": (C.c_char_p, [C.c_int]),
@@ -143,6 +146,10 @@ def lens_flow_step_rescaled(x, v_cond, v_uncond, n_tokens, channels, dt, cfg_sca
                             stream) -> int:
     return lib().lens_flow_step_rescaled(x, v_cond, v_uncond, n_tokens, channels, dt, cfg_scale, x_lowp_out,
                                          lowp_dtype, stream)
+
+
+def lens_quantize_mxfp8(src, src_dtype, rows, cols, q_out, scale_out, stream) -> int:
+    return lib().lens_quantize_mxfp8(src, src_dtype, rows, cols, q_out, scale_out, stream)
 
 
 def lens_timer_start(kind_mask: int) -> int:

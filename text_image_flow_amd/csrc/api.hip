@@ -90,6 +90,9 @@ lens_status check_config(const lens_config *c) {
     return fail(LENS_ERR_UNSUPPORTED, "mlp_hidden %d: must be a positive multiple of 128", c->mlp_hidden);
   if (!(c->eps > 0.f) || !(c->rope_theta > 0.f))
     return fail(LENS_ERR_INVALID_ARG, "eps and rope_theta must be positive");
+  if (c->gemm_fp8 != 0 && c->gemm_fp8 != 1) return fail(LENS_ERR_INVALID_ARG, "gemm_fp8 %d is not 0 or 1", c->gemm_fp8);
+  if (c->gemm_fp8 && c->act_dtype != LENS_BF16)
+    return fail(LENS_ERR_UNSUPPORTED, "gemm_fp8 requires act_dtype LENS_BF16");
   return LENS_OK;
 }
 
@@ -120,15 +123,18 @@ lens_status check_linear(const lens_linear &l, const char *name) {
   return LENS_OK;
 }
 
-lens_status check_block_w(const lens_block_w *w, int idx) {
+lens_status check_block_w(const lens_block_w *w, int idx, bool fp8) {
   if (!w) return fail(LENS_ERR_INVALID_ARG, "block %d weight table is NULL", idx);
   const lens_stream_w *s[2] = {&w->img, &w->txt};
   const char *nm[2] = {"img", "txt"};
   for (int i = 0; i < 2; ++i) {
     const lens_linear *ls[6] = {&s[i]->mod, &s[i]->qkv, &s[i]->out, &s[i]->w1, &s[i]->w3, &s[i]->w2};
     const char *ln[6] = {"mod", "qkv", "out", "w1", "w3", "w2"};
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 6; ++j) {
       if (!ls[j]->w) return fail(LENS_ERR_INVALID_ARG, "block %d %s.%s weight is NULL", idx, nm[i], ln[j]);
+      if (fp8 && j > 0 && !ls[j]->w_scale)
+        return fail(LENS_ERR_INVALID_ARG, "block %d %s.%s: gemm_fp8 needs w_scale", idx, nm[i], ln[j]);
+    }
     if (!s[i]->q_gain || !s[i]->k_gain)
       return fail(LENS_ERR_INVALID_ARG, "block %d %s q/k gain is NULL", idx, nm[i]);
   }
@@ -142,6 +148,9 @@ struct BlockWs {
   void *qkv_img, *qkv_txt;    // [B*S, 3D] act; reused for the SwiGLU output [B*S, mlp]
   void *Q, *K, *V;            // joint layout [B, H, S_pad, 64]
   float2 *rope;               // bf16 path: [S_img + S_txt][32] (cos, sin)
+  // gemm_fp8: MX fp8 copies of a projection's input (e4m3 [B*S, K], E8M0
+  // scales [B*S, K / 32]), K up to max(hidden, mlp_hidden)
+  void *q8_img, *q8_txt, *s8_img, *s8_txt;
   size_t bytes;
 };
 
@@ -168,6 +177,13 @@ BlockWs carve_block(const lens_config *c, int B, int Si, int St, char *base, boo
   w.K = take((size_t)B * c->heads * Sp * 64 * es);
   w.V = take((size_t)B * c->heads * Sp * 64 * es);
   w.rope = (float2 *)take((size_t)(Si + St) * 32 * sizeof(float2));
+  if (c->gemm_fp8) {
+    const size_t kmax = D > (size_t)c->mlp_hidden ? D : (size_t)c->mlp_hidden;
+    w.q8_img = take((size_t)B * Si * kmax);
+    w.q8_txt = take((size_t)B * St * kmax);
+    w.s8_img = take((size_t)B * Si * kmax / 32);
+    w.s8_txt = take((size_t)B * St * kmax / 32);
+  }
   w.bytes = off;
   return w;
 }
@@ -209,6 +225,37 @@ lens_status gemm(lens_kernel_kind, int epi, bool bf, GemmProblem *p, int np, hip
   Timed t(LENS_KERNEL_GEMM, st);
   hipError_t e = t.done(launch_gemm(epi, bf, p, np, st));
   if (e != hipSuccess) return fail(LENS_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
+  return LENS_OK;
+}
+
+// gemm_fp8: MX fp8 copy of the two streams' projection inputs (bf16 [B*S, K])
+lens_status quant_inputs(const void *x_img, const void *x_txt, int64_t Mi, int64_t Mt, int K, const BlockWs &ws,
+                         hipStream_t st) {
+  MxQuantProblem q[2] = {{x_img, ws.q8_img, ws.s8_img, Mi}, {x_txt, ws.q8_txt, ws.s8_txt, Mt}};
+  Timed t(LENS_KERNEL_NORM, st);
+  hipError_t e = t.done(launch_mx_quant(q, 2, K, true, st));
+  if (e != hipSuccess) return fail(LENS_ERR_HIP, "MX fp8 quantization failed: %s", hipGetErrorString(e));
+  return LENS_OK;
+}
+
+// Point both problems of a grouped projection at the MX fp8 inputs and the
+// layers' fp8 weights.
+void to_fp8(GemmProblem *g, const lens_linear &li, const lens_linear &lt, const lens_linear *l3i,
+            const lens_linear *l3t, const BlockWs &ws) {
+  g[0].A = ws.q8_img;
+  g[0].A_scale = ws.s8_img;
+  g[0].W_scale = li.w_scale;
+  g[0].W3_scale = l3i ? l3i->w_scale : nullptr;
+  g[1].A = ws.q8_txt;
+  g[1].A_scale = ws.s8_txt;
+  g[1].W_scale = lt.w_scale;
+  g[1].W3_scale = l3t ? l3t->w_scale : nullptr;
+}
+
+lens_status gemm8(int epi, GemmProblem *p, hipStream_t st, const QkvOut *qo = nullptr) {
+  Timed t(LENS_KERNEL_GEMM, st);
+  hipError_t e = t.done(launch_gemm_fp8(epi, p, 2, st, qo));
+  if (e != hipSuccess) return fail(LENS_ERR_HIP, "fp8 GEMM launch failed: %s", hipGetErrorString(e));
   return LENS_OK;
 }
 
@@ -259,12 +306,19 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   g[0] = GemmProblem{ws.a_img, w->img.qkv.w, nullptr, w->img.qkv.b, nullptr, ws.qkv_img, nullptr, 0, 1, Mi, 3 * D, D};
   g[1] = GemmProblem{ws.a_txt, w->txt.qkv.w, nullptr, w->txt.qkv.b, nullptr, ws.qkv_txt, nullptr, 0, 1, Mt, 3 * D, D};
   const int Sp = s_pad(Si, St);
+  const bool f8 = c->gemm_fp8 != 0;
   if (bf) {
     QkvOut qo{ws.Q, ws.K, ws.V, {w->img.q_gain, w->txt.q_gain}, {w->img.k_gain, w->txt.k_gain}, ws.rope,
               Si, St, Sp, c->heads, c->eps, 0.125f * 1.4426950408889634f};   // attention takes Q in log2 units
-    Timed t(LENS_KERNEL_GEMM, st);
-    e = t.done(launch_gemm(EPI_QKV, true, g, 2, st, &qo));
-    if (e != hipSuccess) return fail(LENS_ERR_HIP, "QKV GEMM launch failed: %s", hipGetErrorString(e));
+    if (f8) {
+      LTRY(quant_inputs(ws.a_img, ws.a_txt, Mi, Mt, D, ws, st));
+      to_fp8(g, w->img.qkv, w->txt.qkv, nullptr, nullptr, ws);
+      LTRY(gemm8(EPI_QKV, g, st, &qo));
+    } else {
+      Timed t(LENS_KERNEL_GEMM, st);
+      e = t.done(launch_gemm(EPI_QKV, true, g, 2, st, &qo));
+      if (e != hipSuccess) return fail(LENS_ERR_HIP, "QKV GEMM launch failed: %s", hipGetErrorString(e));
+    }
   } else {
     LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE, bf, g, 2, st));
     QkRopeArgs qa{ws.qkv_img, ws.qkv_txt, w->img.q_gain, w->img.k_gain, w->txt.q_gain, w->txt.k_gain, img_pos,
@@ -287,7 +341,13 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
                      Mi, D, D};
   g[1] = GemmProblem{ws.a_txt, w->txt.out.w, nullptr, w->txt.out.b, nullptr, h_txt, mod_txt + 2 * D, D6, St > 0 ? St : 1,
                      Mt, D, D};
-  LTRY(gemm(LENS_KERNEL_GEMM, EPI_GATED, bf, g, 2, st));
+  if (f8) {
+    LTRY(quant_inputs(ws.a_img, ws.a_txt, Mi, Mt, D, ws, st));
+    to_fp8(g, w->img.out, w->txt.out, nullptr, nullptr, ws);
+    LTRY(gemm8(EPI_GATED, g, st));
+  } else {
+    LTRY(gemm(LENS_KERNEL_GEMM, EPI_GATED, bf, g, 2, st));
+  }
   // 6. pre-MLP RMSNorm + modulation (shift2, scale2)
   nm[0].shift = mod_img + 3 * D;
   nm[0].scale = mod_img + 4 * D;
@@ -302,13 +362,25 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   const int F = c->mlp_hidden;
   g[0] = GemmProblem{ws.a_img, w->img.w1.w, w->img.w3.w, w->img.w1.b, w->img.w3.b, ws.qkv_img, nullptr, 0, 1, Mi, F, D};
   g[1] = GemmProblem{ws.a_txt, w->txt.w1.w, w->txt.w3.w, w->txt.w1.b, w->txt.w3.b, ws.qkv_txt, nullptr, 0, 1, Mt, F, D};
-  LTRY(gemm(LENS_KERNEL_GEMM, EPI_SWIGLU, bf, g, 2, st));
+  if (f8) {
+    LTRY(quant_inputs(ws.a_img, ws.a_txt, Mi, Mt, D, ws, st));
+    to_fp8(g, w->img.w1, w->txt.w1, &w->img.w3, &w->txt.w3, ws);
+    LTRY(gemm8(EPI_SWIGLU, g, st));
+  } else {
+    LTRY(gemm(LENS_KERNEL_GEMM, EPI_SWIGLU, bf, g, 2, st));
+  }
   // 8. w2 + gated residual (gate2)
   g[0] = GemmProblem{ws.qkv_img, w->img.w2.w, nullptr, w->img.w2.b, nullptr, h_img, mod_img + 5 * D, D6, Si > 0 ? Si : 1,
                      Mi, D, F};
   g[1] = GemmProblem{ws.qkv_txt, w->txt.w2.w, nullptr, w->txt.w2.b, nullptr, h_txt, mod_txt + 5 * D, D6, St > 0 ? St : 1,
                      Mt, D, F};
-  LTRY(gemm(LENS_KERNEL_GEMM, EPI_GATED, bf, g, 2, st));
+  if (f8) {
+    LTRY(quant_inputs(ws.qkv_img, ws.qkv_txt, Mi, Mt, F, ws, st));
+    to_fp8(g, w->img.w2, w->txt.w2, nullptr, nullptr, ws);
+    LTRY(gemm8(EPI_GATED, g, st));
+  } else {
+    LTRY(gemm(LENS_KERNEL_GEMM, EPI_GATED, bf, g, 2, st));
+  }
   return LENS_OK;
 }
 
@@ -365,6 +437,7 @@ void lens_default_config(lens_config *c, lens_dtype act) {
   c->eps = 1e-6f;
   c->t_scale = 1000.f;
   c->act_dtype = act;
+  c->gemm_fp8 = 0;
 }
 
 size_t lens_block_workspace_bytes(const lens_config *c, int32_t B, int32_t Si, int32_t St) {
@@ -383,7 +456,7 @@ lens_status lens_block_forward(const lens_config *c, const lens_block_w *w, floa
                                size_t ws_bytes, void *hip_stream) {
   LTRY(check_config(c));
   LTRY(check_sizes(B, Si, St));
-  LTRY(check_block_w(w, 0));
+  LTRY(check_block_w(w, 0, c->gemm_fp8));
   if (!h_img || !temb || !img_pos) return fail(LENS_ERR_INVALID_ARG, "h_img, temb and img_pos must not be NULL");
   if (St > 0 && (!h_txt || !txt_pos)) return fail(LENS_ERR_INVALID_ARG, "h_txt and txt_pos must not be NULL");
   const BlockWs need = carve_block(c, B, Si, St, nullptr, true);
@@ -414,7 +487,7 @@ lens_status lens_dit_forward(const lens_config *c, const lens_dit_w *w, const vo
   LTRY(check_linear(w->proj_out, "proj_out"));
   if (!w->txt_gain) return fail(LENS_ERR_INVALID_ARG, "txt_gain is NULL");
   if (c->n_blocks > 0 && !w->blocks) return fail(LENS_ERR_INVALID_ARG, "blocks is NULL");
-  for (int i = 0; i < c->n_blocks; ++i) LTRY(check_block_w(&w->blocks[i], i));
+  for (int i = 0; i < c->n_blocks; ++i) LTRY(check_block_w(&w->blocks[i], i, c->gemm_fp8));
   if (!x || !t || !img_pos || !v_out) return fail(LENS_ERR_INVALID_ARG, "x, t, img_pos and v_out must not be NULL");
   if (St > 0 && (!txt_feats || !txt_pos))
     return fail(LENS_ERR_INVALID_ARG, "txt_feats and txt_pos must not be NULL");
@@ -516,6 +589,20 @@ lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *
   if (n_tokens > ((int64_t)1 << 40) / channels) return fail(LENS_ERR_UNSUPPORTED, "too many elements");
   HIP_TRY(launch_flow_step_rescaled(x, v_cond, v_uncond, n_tokens, channels, dt, cfg_scale, x_lowp_out,
                                     lowp_dtype == LENS_BF16, (hipStream_t)hip_stream));
+  return LENS_OK;
+}
+
+lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t rows, int32_t cols, void *q_out,
+                                void *scale_out, void *hip_stream) {
+  if (src_dtype != LENS_F32 && src_dtype != LENS_BF16)
+    return fail(LENS_ERR_INVALID_ARG, "src_dtype %d is not LENS_F32 or LENS_BF16", (int)src_dtype);
+  if (rows < 0 || cols <= 0 || cols % 32)
+    return fail(LENS_ERR_INVALID_ARG, "rows %lld / cols %d: need rows >= 0 and cols a positive multiple of 32",
+                (long long)rows, (int)cols);
+  if (rows > 0 && (!src || !q_out || !scale_out)) return fail(LENS_ERR_INVALID_ARG, "NULL pointer");
+  if (rows > (((int64_t)1 << 40) / cols)) return fail(LENS_ERR_UNSUPPORTED, "too many elements");
+  MxQuantProblem q{src, q_out, scale_out, rows};
+  HIP_TRY(launch_mx_quant(&q, 1, cols, src_dtype == LENS_BF16, (hipStream_t)hip_stream));
   return LENS_OK;
 }
 

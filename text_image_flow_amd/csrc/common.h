@@ -48,6 +48,9 @@ struct GemmProblem {
   int64_t gate_stride;
   int32_t rows_per_gate;
   int32_t M, N, K;
+  // MX fp8 operands (launch_gemm_fp8 only): A, W, W3 hold e4m3 bytes and
+  // these their E8M0 scales, one byte per 32 elements along K ([rows][K/32])
+  const void *A_scale, *W_scale, *W3_scale;
 };
 
 // Outputs of the QKV epilogue.  Problem 0 holds the image rows of the batch
@@ -66,6 +69,23 @@ struct QkvOut {
 // (qo: EPI_QKV only).
 hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream,
                        const QkvOut *qo = nullptr);
+
+// The same grouped GEMM on MX fp8 operands (e4m3 elements, E8M0 scales per
+// 32 along K; K % 128 == 0); the epilogues are those of the bf16 path.
+hipError_t launch_gemm_fp8(int epi, const GemmProblem *probs, int nprob, hipStream_t stream,
+                           const QkvOut *qo = nullptr);
+
+// MX fp8 quantization along rows: src [rows, cols] (bf16 or f32, cols % 32
+// == 0) -> q [rows, cols] e4m3 bytes and scales [rows, cols / 32] E8M0 bytes;
+// per block of 32 the tightest power-of-two scale that keeps every element
+// within +-448, elements rounded to nearest (ties to even).  Up to 2
+// problems in one launch (rows1 = 0 for one).
+struct MxQuantProblem {
+  const void *src;
+  void *q, *scale;
+  int64_t rows;
+};
+hipError_t launch_mx_quant(const MxQuantProblem *p, int nprob, int cols, bool src_bf16, hipStream_t stream);
 
 // RoPE table of the joint sequence: rope[j][i] = (cos, sin) of pos(j)[axis] *
 // theta^(-2 i' / axis_dim) for rotation pair i (pairs 0 .. axes0/2 - 1 on axis

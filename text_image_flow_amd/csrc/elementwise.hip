@@ -536,7 +536,98 @@ __global__ __launch_bounds__(256) void flow_step_rescaled_kernel(float *x, const
   }
 }
 
+// ------------------------------------------------ MX fp8 quantization
+// e4m3 code of y (|y| <= 448, finite), rounded to nearest, ties to even:
+// 3 mantissa bits on normals (exponents -6 .. 8), steps of 2^-9 below 2^-6.
+__device__ __forceinline__ unsigned e4m3_code(float y) {
+  const unsigned u = __float_as_uint(y);
+  const unsigned sign = (u >> 24) & 0x80;
+  const float a = fabsf(y);
+  unsigned code;
+  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9 (8 = the smallest normal)
+    code = (unsigned)rintf(a * 512.0f);      // round-half-even
+  } else {
+    const unsigned au = u & 0x7fffffff;
+    int e = (int)(au >> 23) - 127;
+    unsigned m3 = (au >> 20) & 7, rest = au & 0xfffff;
+    if (rest > 0x80000 || (rest == 0x80000 && (m3 & 1))) ++m3;
+    if (m3 == 8) {
+      m3 = 0;
+      ++e;
+    }
+    code = ((unsigned)(e + 7) << 3) | m3;
+  }
+  return sign | code;
+}
+
+// One thread per 8 consecutive elements; the 4 threads of a 32-block are
+// consecutive lanes.  Scale exponent: the smallest e with amax <= 448 2^e,
+// read off amax's fp32 bits (amax = 1.f 2^E: e = E - 8, plus one when
+// f > 0.75), clamped to [-127, 127]; E8M0 byte = e + 127.
+template <typename T>
+__global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantProblem p0, MxQuantProblem p1, int cols) {
+  const int64_t groups_per_row = cols / 8;
+  const int64_t g0 = p0.rows * groups_per_row;
+  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool second = g >= g0;
+  const MxQuantProblem &p = second ? p1 : p0;
+  if (second) g -= g0;
+  const bool live = g < p.rows * groups_per_row;
+  const int64_t gi = live ? g : 0;
+  float v[8];
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 w = live ? *((const bf16x8 *)p.src + gi) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)w[e];
+  } else {
+    float4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    if (live) {
+      a = *((const float4 *)p.src + 2 * gi);
+      b = *((const float4 *)p.src + 2 * gi + 1);
+    }
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  int ex;
+  if (amax == 0.f) {
+    ex = -127;
+  } else {
+    const unsigned b = __float_as_uint(amax);
+    ex = (int)(b >> 23) - 127 - 8 + ((b & 0x7fffff) > 0x600000 ? 1 : 0);
+    ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+  }
+  if (!live) return;
+  unsigned lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const unsigned c = e4m3_code(ldexpf(v[e], -ex));
+    if (e < 4) lo |= c << (8 * e);
+    else hi |= c << (8 * (e - 4));
+  }
+  *((uint2 *)p.q + gi) = make_uint2(lo, hi);
+  if ((gi & 3) == 0) ((unsigned char *)p.scale)[gi >> 2] = (unsigned char)(ex + 127);
+}
+
 }  // namespace
+
+hipError_t launch_mx_quant(const MxQuantProblem *p, int nprob, int cols, bool src_bf16, hipStream_t stream) {
+  if (cols <= 0 || cols % 32) return hipErrorInvalidValue;
+  MxQuantProblem p1 = nprob > 1 ? p[1] : MxQuantProblem{};
+  if (nprob < 2) p1.rows = 0;
+  const int64_t groups = (p[0].rows + p1.rows) * (cols / 8);
+  if (groups == 0) return hipSuccess;
+  const int64_t blocks = (groups + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (src_bf16)
+    hipLaunchKernelGGL(mx_quant_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, p[0], p1, cols);
+  else
+    hipLaunchKernelGGL(mx_quant_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, p[0], p1, cols);
+  return hipGetLastError();
+}
 
 hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float eps, bool bf16_path,
                                 hipStream_t stream) {

@@ -118,7 +118,7 @@ __device__ __forceinline__ u32x4 pair_runs(unsigned x0, unsigned x1, unsigned y0
 }
 }  // namespace gk
 
-template <int BM, int BN, int WM, int WN, int EPI, int GM, bool BUF = false>
+template <int BM, int BN, int WM, int WN, int EPI, int GM, bool BUF = false, bool F8 = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmProblem p1, int tiles0, int ntm0,
                                                           int ntm1, int total_tiles, int per_xcd, QkvOut qo) {
   using namespace gk;
@@ -135,7 +135,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
   constexpr int ROWS_PER_ROUND = 8 * NW;        // one wave instruction: 8 rows x 128 B
   constexpr int LDA = BM / ROWS_PER_ROUND, LDB = BN / ROWS_PER_ROUND;
   static_assert(LDA * ROWS_PER_ROUND == BM && LDB * ROWS_PER_ROUND == BN, "rows must split over waves");
-  constexpr int KS = RBK / 16;                  // MFMA k steps per slab
+  static_assert(!F8 || BUF, "fp8 operands use buffer loads");
+  constexpr int ES = F8 ? 1 : 2;                // bytes per element
+  constexpr int SLAB_K = RROW / ES;             // k per slab (one 128-byte line per row)
+  constexpr int KS = SLAB_K / (F8 ? 64 : 16);   // MFMA k steps per slab
   static_assert(LDB % (KS / 2) == 0 && LDA % (KS / 2) == 0, "load parts must split over half the steps");
   constexpr int PB = LDB / (KS / 2), PA = LDA / (KS / 2);
   constexpr int SMEM = NA * A_UNIT + NB * B_UNIT;
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
   const int ntn = p0.N / OUTC;
-  const int K = p0.K, KT = K / RBK;
+  const int K = p0.K, KT = K / SLAB_K;
   const int lrow = lane >> 3, lslot = lane & 7;
   const int dst0 = wave * 8 * RROW;             // wave's rows inside a round
 
@@ -179,12 +182,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
     _Pragma("unroll") for (int i = 0; i < LDA; ++i) {                                                     \
       const int r = i * ROWS_PER_ROUND + wave * 8 + lrow;                                                 \
       const int gr = m0_ + r < M_ ? m0_ + r : M_ - 1;                                                     \
-      if constexpr (BUF) a_off[i] = (gr * K + (lslot ^ swz(r)) * 8) * 2;                                  \
+      if constexpr (BUF) a_off[i] = (int)__umul24(gr, K * ES) + (lslot ^ swz(r)) * 16;                    \
       else a_src[i] = A_ + (int64_t)gr * K + (lslot ^ swz(r)) * 8;                                        \
     }                                                                                                     \
     if constexpr (BUF) {                                                                                  \
       a_base = A_;                                                                                        \
-      a_bytes = M_ * K * 2;                                                                               \
+      a_bytes = M_ * K * ES;                                                                              \
     }                                                                                                     \
   } while (0)
 #define B_SETUP(t_)                                                                                       \
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
       const int r = i * ROWS_PER_ROUND + wave * 8 + lrow;                                                 \
       if constexpr (BUF) {                                                                                \
         const int wr_ = SWI && r >= BN / 2 ? r - BN / 2 : r;                                              \
-        b_off[i] = ((n0_ + wr_) * K + (lslot ^ swz(r)) * 8) * 2;                                          \
+        b_off[i] = (int)__umul24(n0_ + wr_, K * ES) + (lslot ^ swz(r)) * 16;                              \
       } else {                                                                                            \
         const bf16 *base_;                                                                                \
         if constexpr (SWI) {                                                                              \
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
     if constexpr (BUF) {                                                                                  \
       b_base = W_;                                                                                        \
       b3_base = W3_;                                                                                      \
-      b_bytes = N_ * K * 2;                                                                               \
+      b_bytes = N_ * K * ES;                                                                              \
     }                                                                                                     \
   } while (0)
 // one load instruction (part i) of the current A / W slab, and the cursor
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
   do {                                                                                                     \
     lds_void *d_ = (lds_void *)(a_ring + apos * A_UNIT + dst0 + (i_) * ROWS_PER_ROUND * RROW);             \
     if constexpr (BUF)                                                                                     \
-      buffer_lds16(a_base, a_bytes, d_, a_off[i_], akt * RBK * 2);                                         \
+      buffer_lds16(a_base, a_bytes, d_, a_off[i_], akt * RROW);                                            \
     else                                                                                                   \
       __builtin_amdgcn_global_load_lds((const void *)(a_src[i_] + akt * RBK), d_, 16, 0, 0);               \
   } while (0)
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
     lds_void *d_ = (lds_void *)(b_ring + bpos * B_UNIT + dst0 + (i_) * ROWS_PER_ROUND * RROW);             \
     if constexpr (BUF) {                                                                                   \
       const void *bb_ = SWI && (i_) * ROWS_PER_ROUND >= BN / 2 ? b3_base : b_base;                        \
-      buffer_lds16(bb_, b_bytes, d_, b_off[i_], bkt * RBK * 2);                                            \
+      buffer_lds16(bb_, b_bytes, d_, b_off[i_], bkt * RROW);                                               \
     } else {                                                                                               \
       __builtin_amdgcn_global_load_lds((const void *)(b_src[i_] + bkt * RBK), d_, 16, 0, 0);               \
     }                                                                                                      \
@@ -302,7 +305,57 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
 
+    // fp8: this tile's scale rows (one dword = the 4 E8M0 bytes of a slab),
+    // the current slab's dwords and the next slab's, loaded one slab ahead
+    // (raw buffer loads: one 32-bit row offset per fragment, the slab in
+    // the scalar offset)
+    int so_a[F8 ? MT : 1], so_w[F8 ? NT : 1];
+    unsigned s_a[F8 ? MT : 1], s_w[F8 ? NT : 1], n_a[F8 ? MT : 1], n_w[F8 ? NT : 1];
+    __amdgpu_buffer_rsrc_t rs_a, rs_w, rs_w3;
+    if constexpr (F8) {
+      bool sec_;
+      int m0_, n0_;
+      tile_coords(ct, tiles0, ntm0, ntm1, ntn, GM, BM, OUTC, sec_, m0_, n0_);
+      const GemmProblem &pp = sec_ ? p1 : p0;
+      const int kb = K / 32;                    // scale bytes per row
+      rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)pp.A_scale, (short)0, pp.M * kb, 0x00020000);
+      rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)pp.W_scale, (short)0, pp.N * kb, 0x00020000);
+      rs_w3 = __builtin_amdgcn_make_buffer_rsrc((void *)(SWI ? pp.W3_scale : pp.W_scale), (short)0, pp.N * kb,
+                                                0x00020000);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) so_a[i] = min(m0_ + a_row[i], pp.M - 1) * kb;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const bool third = SWI && b_row[j] >= BN / 2;
+        so_w[j] = (n0_ + (third ? b_row[j] - BN / 2 : b_row[j])) * kb;
+      }
+      // lanes of the upper half take blocks 1 and 3 of a slab: shift them down
+#pragma unroll
+      for (int i = 0; i < MT; ++i) n_a[i] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rs_a, so_a[i], 0, 0) >> (8 * hl);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        n_w[j] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(SWI && b_row[j] >= BN / 2 ? rs_w3 : rs_w, so_w[j], 0, 0) >> (8 * hl);
+    }
+
     for (int kt = 0; kt < KT; ++kt) {
+      if constexpr (F8) {
+        // this slab's scales (loaded during the previous slab), then the
+        // next slab's, issued before this iteration's W parts so that the
+        // slab wait at the top of the next iteration already covers them
+#pragma unroll
+        for (int i = 0; i < MT; ++i) s_a[i] = n_a[i];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) s_w[j] = n_w[j];
+        if (kt + 1 < KT) {
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+            n_a[i] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rs_a, so_a[i], (kt + 1) * 4, 0) >> (8 * hl);
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            n_w[j] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(SWI && b_row[j] >= BN / 2 ? rs_w3 : rs_w, so_w[j],
+                                                                    (kt + 1) * 4, 0) >> (8 * hl);
+        }
+      }
       if (a_issued > consumed + 1) wait_vm<LDA>();
       else wait_vm<0>();
       // Barrier without a memory fence: the wait covers this wave's slab
@@ -315,6 +368,59 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
       const bool do_b = bt < t_end, do_a = at < t_end;
       const char *sa = a_ring + ca * A_UNIT;
       const char *sb = b_ring + cb * B_UNIT;
+      if constexpr (F8) {
+        // k step ks covers k 64 ks .. 64 ks + 63 of the slab; lane half hl
+        // supplies the 16-byte chunks 4 ks + hl and 4 ks + 2 + hl of its row
+        // (the MFMA's k order: bytes j of lane l are k = 32 (j / 16) +
+        // 16 (l / 32) + j % 16), and byte 2 ks of its scale dword is the
+        // scale of block 2 ks + hl.
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          typedef int i32x8 __attribute__((ext_vector_type(8)));
+          i32x8 fa8[MT / 2], fb8[NT];
+          const int c0 = ks * 4 + hl, c1 = ks * 4 + 2 + hl;
+#define F8_FRAG(dst_, base_, row_)                                                                         \
+  do {                                                                                                     \
+    const u32x4 lo_ = *(const u32x4 *)((base_) + (row_) * RROW + ((c0 ^ swz(row_)) << 4));                  \
+    const u32x4 hi_ = *(const u32x4 *)((base_) + (row_) * RROW + ((c1 ^ swz(row_)) << 4));                  \
+    dst_ = i32x8{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3], (int)hi_[0], (int)hi_[1], (int)hi_[2], \
+                 (int)hi_[3]};                                                                             \
+  } while (0)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) F8_FRAG(fb8[j], sb, b_row[j]);
+          if (ks < KS / 2) {
+            if (do_b) {
+#pragma unroll
+              for (int i = ks * PB; i < (ks + 1) * PB; ++i) ISSUE_B_PART(i);
+            }
+          } else {
+            if (do_a) {
+#pragma unroll
+              for (int i = (ks - KS / 2) * PA; i < (ks - KS / 2 + 1) * PA; ++i) ISSUE_A_PART(i);
+            }
+          }
+          // the A fragments in two halves (registers: 8 VGPRs per fragment)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+            for (int i = 0; i < MT / 2; ++i) F8_FRAG(fa8[i], sa, a_row[h2 * (MT / 2) + i]);
+#pragma unroll
+            for (int i = 0; i < MT / 2; ++i)
+#pragma unroll
+              for (int j = 0; j < NT; ++j) {
+                const int ii = h2 * (MT / 2) + i;
+                if (ks == 0)
+                  acc[ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[j], fa8[i], acc[ii][j], 0, 0, 0,
+                                                                               (int)s_w[j], 0, (int)s_a[ii]);
+                else
+                  acc[ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[j], fa8[i], acc[ii][j], 0, 0, 2,
+                                                                               (int)s_w[j], 2, (int)s_a[ii]);
+              }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#undef F8_FRAG
+        }
+      } else {
       bf16x8 fa[2][MT], fb[2][NT];
 #define READ_FRAGS(buf_, ks_)                                                                              \
   do {                                                                                                     \
@@ -347,6 +453,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
       }
 #undef READ_FRAGS
+      }
       if (do_b) STEP_B();
       if (do_a) STEP_A();
       ca = ca + 1 == NA ? 0 : ca + 1;
@@ -567,11 +674,16 @@ int cu_count() {
 // Both problems of a grouped launch must share N and K (the image and text
 // weights of one layer do); N must be a multiple of the tile's output
 // columns and K of the slab depth.
-template <int BM, int BN, int WM, int WN, int EPI, int GM = 4, bool BUF = false>
+template <int BM, int BN, int WM, int WN, int EPI, int GM = 4, bool BUF = false, bool F8 = false>
 hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st, const QkvOut *qo = nullptr, int max_grid = 0) {
   const int outc = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   if (np > 1 && (pr[0].N != pr[1].N || pr[0].K != pr[1].K)) return hipErrorInvalidValue;
-  if (pr[0].N % outc || pr[0].K % gk::RBK || pr[0].K <= 0) return hipErrorInvalidValue;
+  if (pr[0].N % outc || pr[0].K % (F8 ? 128 : gk::RBK) || pr[0].K <= 0) return hipErrorInvalidValue;
+  if constexpr (F8) {
+    for (int i = 0; i < np; ++i)
+      if (pr[i].M > 0 && (!pr[i].A_scale || !pr[i].W_scale || (EPI == EPI_SWIGLU && !pr[i].W3_scale)))
+        return hipErrorInvalidValue;
+  }
   int ntm[2] = {0, 0}, tiles[2] = {0, 0};
   for (int i = 0; i < np; ++i) {
     ntm[i] = (pr[i].M + BM - 1) / BM;
@@ -589,7 +701,7 @@ hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st, const QkvOut 
     if (!qo) return hipErrorInvalidValue;
     qv = *qo;
   }
-  hipLaunchKernelGGL((gemm_bf16<BM, BN, WM, WN, EPI, GM, BUF>), dim3(grid), dim3(64 * WM * WN), 0, st, q0, q1, tiles[0],
+  hipLaunchKernelGGL((gemm_bf16<BM, BN, WM, WN, EPI, GM, BUF, F8>), dim3(grid), dim3(64 * WM * WN), 0, st, q0, q1, tiles[0],
                      ntm[0] > 0 ? ntm[0] : 1, ntm[1] > 0 ? ntm[1] : 1, total, per_xcd, qv);
   return hipGetLastError();
 }
@@ -690,6 +802,34 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st, const Qk
   if (tiles256 * 2 < cu_count())
     return buf ? run_bf16<128, 256, 2, 4, EPI, 4, true>(pr, np, st, qo) : run_bf16<128, 256, 2, 4, EPI>(pr, np, st, qo);
   return buf ? run_bf16<256, 256, 2, 4, EPI, 4, true>(pr, np, st, qo) : run_bf16<256, 256, 2, 4, EPI>(pr, np, st, qo);
+}
+
+// fp8: 128 x 256 tiles (a 256 x 256 fp8 tile does not fit the 256-VGPR
+// budget of two waves per SIMD with its fragments and scales); every
+// operand must be below 2 GiB (buffer loads)
+template <int EPI>
+hipError_t dispatch_fp8(const GemmProblem *pr, int np, hipStream_t st, const QkvOut *qo) {
+  constexpr bool SWI = EPI == EPI_SWIGLU;
+  const int outc = SWI ? 128 : 256;
+  int tiles256 = 0;
+  for (int i = 0; i < np; ++i) {
+    if (pr[i].N % outc) return hipErrorInvalidValue;
+    if ((int64_t)pr[i].M * pr[i].K >= (int64_t(1) << 31) || (int64_t)pr[i].N * pr[i].K >= (int64_t(1) << 31))
+      return hipErrorInvalidValue;
+    tiles256 += ((pr[i].M + 255) / 256) * (pr[i].N / outc);
+  }
+  (void)tiles256;
+  return run_bf16<128, 256, 2, 4, EPI, 4, true, true>(pr, np, st, qo);
+}
+
+hipError_t launch_gemm_fp8(int epi, const GemmProblem *probs, int nprob, hipStream_t stream, const QkvOut *qo) {
+  switch (epi) {
+    case EPI_STORE: return dispatch_fp8<EPI_STORE>(probs, nprob, stream, nullptr);
+    case EPI_GATED: return dispatch_fp8<EPI_GATED>(probs, nprob, stream, nullptr);
+    case EPI_SWIGLU: return dispatch_fp8<EPI_SWIGLU>(probs, nprob, stream, nullptr);
+    case EPI_QKV: return dispatch_fp8<EPI_QKV>(probs, nprob, stream, qo);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream,

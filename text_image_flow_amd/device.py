@@ -46,12 +46,50 @@ def stream_handle(stream=None) -> int:
     return s.cuda_stream
 
 
-class DeviceBlock:
-    """One block's weights on the device plus its lens_block_w table."""
+FP8_LINEARS = ("qkv", "out", "w1", "w3", "w2")   # the projections an MX fp8 model quantizes
 
-    def __init__(self, w: dict, act_dtype: int, device="cuda"):
+
+def quantize_mxfp8(w: torch.Tensor, stream=None):
+    """MX fp8 copy of a bf16 / f32 device matrix [rows, cols] (lens_quantize_mxfp8):
+    -> (e4m3 bytes [rows, cols] uint8, E8M0 scales [rows, cols / 32] uint8)."""
+    rows, cols = w.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
+    dt = L.LENS_BF16 if w.dtype == torch.bfloat16 else L.LENS_F32
+    L.check(L.lens_quantize_mxfp8(ptr(w), dt, rows, cols, ptr(q), ptr(s), stream_handle(stream)))
+    return q, s
+
+
+class DeviceBlock:
+    """One block's weights on the device plus its lens_block_w table.  With
+    gemm_fp8 the projections in FP8_LINEARS are stored as MX fp8 (quantized
+    on the device from the act_dtype upload)."""
+
+    def __init__(self, w: dict, act_dtype: int, device="cuda", gemm_fp8: bool = False):
         self.t = {s: {k: upload(v, act_dtype, device) if v is not None else None for k, v in w[s].items()}
                   for s in STREAMS}
+        if gemm_fp8:
+            for s in STREAMS:
+                for name in FP8_LINEARS:
+                    q, sc = quantize_mxfp8(self.t[s][f"{name}_w"])
+                    self.t[s][f"{name}_w"], self.t[s][f"{name}_s"] = q, sc
+            torch.cuda.synchronize(device)
+        self._table()
+
+    @classmethod
+    def fp8_copy(cls, blk: "DeviceBlock") -> "DeviceBlock":
+        """An MX fp8 version of a bf16 device block, quantized on the device
+        (biases, gains and the AdaLN weight are shared, not copied)."""
+        new = object.__new__(cls)
+        new.t = {s: dict(blk.t[s]) for s in STREAMS}
+        for s in STREAMS:
+            for name in FP8_LINEARS:
+                new.t[s][f"{name}_w"], new.t[s][f"{name}_s"] = quantize_mxfp8(blk.t[s][f"{name}_w"])
+        torch.cuda.synchronize()
+        new._table()
+        return new
+
+    def _table(self):
         self.table = L.LensBlockW()
         for s in STREAMS:
             sw = getattr(self.table, s)
@@ -59,6 +97,7 @@ class DeviceBlock:
                 lin = getattr(sw, name)
                 lin.w = ptr(self.t[s][f"{name}_w"])
                 lin.b = ptr(self.t[s].get(f"{name}_b"))
+                lin.w_scale = ptr(self.t[s].get(f"{name}_s"))
             sw.q_gain = ptr(self.t[s]["q_gain"])
             sw.k_gain = ptr(self.t[s]["k_gain"])
 
@@ -66,9 +105,10 @@ class DeviceBlock:
 class DeviceDit:
     """All denoiser weights on the device plus the lens_dit_w table."""
 
-    def __init__(self, top: dict, blocks, act_dtype: int, device="cuda"):
+    def __init__(self, top: dict, blocks, act_dtype: int, device="cuda", gemm_fp8: bool = False):
         self.top = {k: upload(v, act_dtype, device) if v is not None else None for k, v in top.items()}
-        self.blocks = [b if isinstance(b, DeviceBlock) else DeviceBlock(b, act_dtype, device) for b in blocks]
+        self.blocks = [b if isinstance(b, DeviceBlock) else DeviceBlock(b, act_dtype, device, gemm_fp8)
+                       for b in blocks]
         self._tables()
 
     def with_blocks(self, order):
