@@ -373,21 +373,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
         // supplies the 16-byte chunks 4 ks + hl and 4 ks + 2 + hl of its row
         // (the MFMA's k order: bytes j of lane l are k = 32 (j / 16) +
         // 16 (l / 32) + j % 16), and byte 2 ks of its scale dword is the
-        // scale of block 2 ks + hl.
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          typedef int i32x8 __attribute__((ext_vector_type(8)));
-          i32x8 fa8[MT / 2], fb8[NT];
-          const int c0 = ks * 4 + hl, c1 = ks * 4 + 2 + hl;
-#define F8_FRAG(dst_, base_, row_)                                                                         \
+        // scale of block 2 ks + hl.  Fragments are read one A row tile
+        // ahead and the next step's W tiles one step ahead; the empty asm
+        // after each MFMA keeps it in place (otherwise the MFMAs drift
+        // below the load bookkeeping and every fragment of the slab is
+        // live at once, which spills the 256-row tile).
+        typedef int i32x8 __attribute__((ext_vector_type(8)));
+        i32x8 fa8[2], fb8[2][NT];
+#define F8_FRAG(dst_, base_, row_, ks_)                                                                    \
   do {                                                                                                     \
-    const u32x4 lo_ = *(const u32x4 *)((base_) + (row_) * RROW + ((c0 ^ swz(row_)) << 4));                  \
-    const u32x4 hi_ = *(const u32x4 *)((base_) + (row_) * RROW + ((c1 ^ swz(row_)) << 4));                  \
+    const int c0_ = (ks_) * 4 + hl, c1_ = (ks_) * 4 + 2 + hl;                                              \
+    const u32x4 lo_ = *(const u32x4 *)((base_) + (row_) * RROW + ((c0_ ^ swz(row_)) << 4));                 \
+    const u32x4 hi_ = *(const u32x4 *)((base_) + (row_) * RROW + ((c1_ ^ swz(row_)) << 4));                 \
     dst_ = i32x8{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3], (int)hi_[0], (int)hi_[1], (int)hi_[2], \
                  (int)hi_[3]};                                                                             \
   } while (0)
 #pragma unroll
-          for (int j = 0; j < NT; ++j) F8_FRAG(fb8[j], sb, b_row[j]);
+        for (int j = 0; j < NT; ++j) F8_FRAG(fb8[0][j], sb, b_row[j], 0);
+        F8_FRAG(fa8[0], sa, a_row[0], 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int cur = ks & 1;
           if (ks < KS / 2) {
             if (do_b) {
 #pragma unroll
@@ -399,27 +405,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
               for (int i = (ks - KS / 2) * PA; i < (ks - KS / 2 + 1) * PA; ++i) ISSUE_A_PART(i);
             }
           }
-          // the A fragments in two halves (registers: 8 VGPRs per fragment)
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
+          for (int i = 0; i < MT; ++i) {
+            if (i + 1 < MT) F8_FRAG(fa8[(i + 1) & 1], sa, a_row[i + 1], ks);
+            else if (ks + 1 < KS) F8_FRAG(fa8[0], sa, a_row[0], ks + 1);
+            if (i == 0 && ks + 1 < KS) {
 #pragma unroll
-            for (int i = 0; i < MT / 2; ++i) F8_FRAG(fa8[i], sa, a_row[h2 * (MT / 2) + i]);
-#pragma unroll
-            for (int i = 0; i < MT / 2; ++i)
-#pragma unroll
-              for (int j = 0; j < NT; ++j) {
-                const int ii = h2 * (MT / 2) + i;
-                if (ks == 0)
-                  acc[ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[j], fa8[i], acc[ii][j], 0, 0, 0,
-                                                                               (int)s_w[j], 0, (int)s_a[ii]);
-                else
-                  acc[ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[j], fa8[i], acc[ii][j], 0, 0, 2,
-                                                                               (int)s_w[j], 2, (int)s_a[ii]);
-              }
+              for (int j = 0; j < NT; ++j) F8_FRAG(fb8[cur ^ 1][j], sb, b_row[j], ks + 1);
+            }
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              if (ks == 0)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[cur][j], fa8[i & 1], acc[i][j], 0, 0,
+                                                                            0, (int)s_w[j], 0, (int)s_a[i]);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[cur][j], fa8[i & 1], acc[i][j], 0, 0,
+                                                                            2, (int)s_w[j], 2, (int)s_a[i]);
+              asm volatile("" : "+v"(acc[i][j]));
+            }
           }
-#undef F8_FRAG
         }
+#undef F8_FRAG
       } else {
       bf16x8 fa[2][MT], fb[2][NT];
 #define READ_FRAGS(buf_, ks_)                                                                              \
@@ -804,9 +811,9 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st, const Qk
   return buf ? run_bf16<256, 256, 2, 4, EPI, 4, true>(pr, np, st, qo) : run_bf16<256, 256, 2, 4, EPI>(pr, np, st, qo);
 }
 
-// fp8: 128 x 256 tiles (a 256 x 256 fp8 tile does not fit the 256-VGPR
-// budget of two waves per SIMD with its fragments and scales); every
-// operand must be below 2 GiB (buffer loads)
+// fp8: the bf16 tile choice (256 x 256, or 128 x 256 when 256-row tiles
+// would leave most CUs idle); every operand must be below 2 GiB (buffer
+// loads)
 template <int EPI>
 hipError_t dispatch_fp8(const GemmProblem *pr, int np, hipStream_t st, const QkvOut *qo) {
   constexpr bool SWI = EPI == EPI_SWIGLU;
@@ -818,8 +825,8 @@ hipError_t dispatch_fp8(const GemmProblem *pr, int np, hipStream_t st, const Qkv
       return hipErrorInvalidValue;
     tiles256 += ((pr[i].M + 255) / 256) * (pr[i].N / outc);
   }
-  (void)tiles256;
-  return run_bf16<128, 256, 2, 4, EPI, 4, true, true>(pr, np, st, qo);
+  if (tiles256 * 2 < cu_count()) return run_bf16<128, 256, 2, 4, EPI, 4, true, true>(pr, np, st, qo);
+  return run_bf16<256, 256, 2, 4, EPI, 4, true, true>(pr, np, st, qo);
 }
 
 hipError_t launch_gemm_fp8(int epi, const GemmProblem *probs, int nprob, hipStream_t stream, const QkvOut *qo) {
