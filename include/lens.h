@@ -79,7 +79,11 @@ typedef struct {
   lens_dtype act_dtype; /* element type of weights and activations */
   int32_t gemm_fp8;     /* 1: the block projections qkv, out, w1, w3, w2 run as
                            MX fp8 GEMMs (requires act_dtype LENS_BF16; see
-                           lens_quantize_mxfp8); 0 (default): act_dtype */
+                           lens_quantize_mxfp8): their inputs are quantized
+                           from fp32 by the kernels that produce them (the
+                           two norms, attention, the SwiGLU epilogue), with
+                           the same rule as lens_quantize_mxfp8;
+                           0 (default): act_dtype */
 } lens_config;
 
 /* One Linear layer: w [out, in] in act_dtype, b [out] in act_dtype or NULL.
@@ -230,7 +234,7 @@ lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t r
 typedef enum {
   LENS_KERNEL_GEMM = 0,        /* bf16 MFMA GEMM (all projections) */
   LENS_KERNEL_ATTENTION = 1,   /* joint flash attention */
-  LENS_KERNEL_NORM = 2,        /* RMSNorm + modulation; MX fp8 activation quantization */
+  LENS_KERNEL_NORM = 2,        /* RMSNorm + modulation (bf16 or MX fp8 output) */
   LENS_KERNEL_QKNORM_ROPE = 3, /* QK RMSNorm + RoPE + joint layout */
   LENS_KERNEL_ADALN = 4,       /* skinny GEMV (AdaLN, timestep MLP) */
   LENS_KERNEL_COUNT = 5

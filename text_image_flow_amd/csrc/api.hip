@@ -148,9 +148,11 @@ struct BlockWs {
   void *qkv_img, *qkv_txt;    // [B*S, 3D] act; reused for the SwiGLU output [B*S, mlp]
   void *Q, *K, *V;            // joint layout [B, H, S_pad, 64]
   float2 *rope;               // bf16 path: [S_img + S_txt][32] (cos, sin)
-  // gemm_fp8: MX fp8 copies of a projection's input (e4m3 [B*S, K], E8M0
-  // scales [B*S, K / 32]), K up to max(hidden, mlp_hidden)
+  // gemm_fp8: the projections' inputs as MX fp8 (e4m3 rows, E8M0 scales
+  // [rows, K / 32]): q8/s8 [B*S, hidden] from the norms and the attention,
+  // f8/fs8 [B*S, mlp_hidden] from the SwiGLU epilogue
   void *q8_img, *q8_txt, *s8_img, *s8_txt;
+  void *f8_img, *f8_txt, *fs8_img, *fs8_txt;
   size_t bytes;
 };
 
@@ -178,11 +180,15 @@ BlockWs carve_block(const lens_config *c, int B, int Si, int St, char *base, boo
   w.V = take((size_t)B * c->heads * Sp * 64 * es);
   w.rope = (float2 *)take((size_t)(Si + St) * 32 * sizeof(float2));
   if (c->gemm_fp8) {
-    const size_t kmax = D > (size_t)c->mlp_hidden ? D : (size_t)c->mlp_hidden;
-    w.q8_img = take((size_t)B * Si * kmax);
-    w.q8_txt = take((size_t)B * St * kmax);
-    w.s8_img = take((size_t)B * Si * kmax / 32);
-    w.s8_txt = take((size_t)B * St * kmax / 32);
+    const size_t F = (size_t)c->mlp_hidden;
+    w.q8_img = take((size_t)B * Si * D);
+    w.q8_txt = take((size_t)B * St * D);
+    w.s8_img = take((size_t)B * Si * D / 32);
+    w.s8_txt = take((size_t)B * St * D / 32);
+    w.f8_img = take((size_t)B * Si * F);
+    w.f8_txt = take((size_t)B * St * F);
+    w.fs8_img = take((size_t)B * Si * F / 32);
+    w.fs8_txt = take((size_t)B * St * F / 32);
   }
   w.bytes = off;
   return w;
@@ -228,26 +234,16 @@ lens_status gemm(lens_kernel_kind, int epi, bool bf, GemmProblem *p, int np, hip
   return LENS_OK;
 }
 
-// gemm_fp8: MX fp8 copy of the two streams' projection inputs (bf16 [B*S, K])
-lens_status quant_inputs(const void *x_img, const void *x_txt, int64_t Mi, int64_t Mt, int K, const BlockWs &ws,
-                         hipStream_t st) {
-  MxQuantProblem q[2] = {{x_img, ws.q8_img, ws.s8_img, Mi}, {x_txt, ws.q8_txt, ws.s8_txt, Mt}};
-  Timed t(LENS_KERNEL_NORM, st);
-  hipError_t e = t.done(launch_mx_quant(q, 2, K, true, st));
-  if (e != hipSuccess) return fail(LENS_ERR_HIP, "MX fp8 quantization failed: %s", hipGetErrorString(e));
-  return LENS_OK;
-}
-
-// Point both problems of a grouped projection at the MX fp8 inputs and the
-// layers' fp8 weights.
+// Point both problems of a grouped projection at MX fp8 inputs (x8/xs8 of
+// the image and text rows) and the layers' fp8 weights.
 void to_fp8(GemmProblem *g, const lens_linear &li, const lens_linear &lt, const lens_linear *l3i,
-            const lens_linear *l3t, const BlockWs &ws) {
-  g[0].A = ws.q8_img;
-  g[0].A_scale = ws.s8_img;
+            const lens_linear *l3t, void *x8_img, void *xs8_img, void *x8_txt, void *xs8_txt) {
+  g[0].A = x8_img;
+  g[0].A_scale = xs8_img;
   g[0].W_scale = li.w_scale;
   g[0].W3_scale = l3i ? l3i->w_scale : nullptr;
-  g[1].A = ws.q8_txt;
-  g[1].A_scale = ws.s8_txt;
+  g[1].A = x8_txt;
+  g[1].A_scale = xs8_txt;
   g[1].W_scale = lt.w_scale;
   g[1].W3_scale = l3t ? l3t->w_scale : nullptr;
 }
@@ -289,13 +285,16 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   const int Mi = B * Si, Mt = B * St;
   hipError_t e;
 
+  // gemm_fp8: every projection input is produced as MX fp8 by the kernel
+  // before it (norms, attention, SwiGLU epilogue), never stored as bf16
+  const bool f8 = c->gemm_fp8 != 0;
   // 1. pre-attention RMSNorm + modulation (shift1, scale1)
   NormModProblem nm[2] = {
-      {h_img, ws.a_img, mod_img, mod_img + D, D6, Mi, Si > 0 ? Si : 1},
-      {h_txt, ws.a_txt, mod_txt, mod_txt + D, D6, Mt, St > 0 ? St : 1}};
+      {h_img, f8 ? ws.q8_img : ws.a_img, mod_img, mod_img + D, D6, Mi, Si > 0 ? Si : 1, ws.s8_img},
+      {h_txt, f8 ? ws.q8_txt : ws.a_txt, mod_txt, mod_txt + D, D6, Mt, St > 0 ? St : 1, ws.s8_txt}};
   {
     Timed t(LENS_KERNEL_NORM, st);
-    e = t.done(launch_norm_modulate(nm, 2, D, c->eps, bf, st));
+    e = t.done(launch_norm_modulate(nm, 2, D, c->eps, bf, st, f8));
     if (e != hipSuccess) return fail(LENS_ERR_HIP, "norm launch failed: %s", hipGetErrorString(e));
   }
   // 2. QKV projections, 3. QK RMSNorm + RoPE -> joint Q, K, V.  bf16: one
@@ -306,13 +305,11 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   g[0] = GemmProblem{ws.a_img, w->img.qkv.w, nullptr, w->img.qkv.b, nullptr, ws.qkv_img, nullptr, 0, 1, Mi, 3 * D, D};
   g[1] = GemmProblem{ws.a_txt, w->txt.qkv.w, nullptr, w->txt.qkv.b, nullptr, ws.qkv_txt, nullptr, 0, 1, Mt, 3 * D, D};
   const int Sp = s_pad(Si, St);
-  const bool f8 = c->gemm_fp8 != 0;
   if (bf) {
     QkvOut qo{ws.Q, ws.K, ws.V, {w->img.q_gain, w->txt.q_gain}, {w->img.k_gain, w->txt.k_gain}, ws.rope,
               Si, St, Sp, c->heads, c->eps, 0.125f * 1.4426950408889634f};   // attention takes Q in log2 units
     if (f8) {
-      LTRY(quant_inputs(ws.a_img, ws.a_txt, Mi, Mt, D, ws, st));
-      to_fp8(g, w->img.qkv, w->txt.qkv, nullptr, nullptr, ws);
+      to_fp8(g, w->img.qkv, w->txt.qkv, nullptr, nullptr, ws.q8_img, ws.s8_img, ws.q8_txt, ws.s8_txt);
       LTRY(gemm8(EPI_QKV, g, st, &qo));
     } else {
       Timed t(LENS_KERNEL_GEMM, st);
@@ -331,6 +328,12 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   // 4. joint attention; outputs overwrite the (dead) norm outputs
   AttnArgs aa{ws.Q, ws.K, ws.V, ws.a_img, ws.a_txt, txt_len, B, c->heads, Si, St, Sp, 0.125f,
               {w->img.q_gain, w->img.k_gain, w->txt.q_gain, w->txt.k_gain}};
+  if (f8) {
+    aa.O8_img = ws.q8_img;
+    aa.O8_txt = ws.q8_txt;
+    aa.OS_img = ws.s8_img;
+    aa.OS_txt = ws.s8_txt;
+  }
   {
     Timed t(LENS_KERNEL_ATTENTION, st);
     e = t.done(launch_attention(aa, bf, st));
@@ -342,8 +345,7 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   g[1] = GemmProblem{ws.a_txt, w->txt.out.w, nullptr, w->txt.out.b, nullptr, h_txt, mod_txt + 2 * D, D6, St > 0 ? St : 1,
                      Mt, D, D};
   if (f8) {
-    LTRY(quant_inputs(ws.a_img, ws.a_txt, Mi, Mt, D, ws, st));
-    to_fp8(g, w->img.out, w->txt.out, nullptr, nullptr, ws);
+    to_fp8(g, w->img.out, w->txt.out, nullptr, nullptr, ws.q8_img, ws.s8_img, ws.q8_txt, ws.s8_txt);
     LTRY(gemm8(EPI_GATED, g, st));
   } else {
     LTRY(gemm(LENS_KERNEL_GEMM, EPI_GATED, bf, g, 2, st));
@@ -355,7 +357,7 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   nm[1].scale = mod_txt + 4 * D;
   {
     Timed t(LENS_KERNEL_NORM, st);
-    e = t.done(launch_norm_modulate(nm, 2, D, c->eps, bf, st));
+    e = t.done(launch_norm_modulate(nm, 2, D, c->eps, bf, st, f8));
     if (e != hipSuccess) return fail(LENS_ERR_HIP, "norm launch failed: %s", hipGetErrorString(e));
   }
   // 7. w1 | w3 with the SwiGLU epilogue (output reuses the qkv buffers)
@@ -363,9 +365,12 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   g[0] = GemmProblem{ws.a_img, w->img.w1.w, w->img.w3.w, w->img.w1.b, w->img.w3.b, ws.qkv_img, nullptr, 0, 1, Mi, F, D};
   g[1] = GemmProblem{ws.a_txt, w->txt.w1.w, w->txt.w3.w, w->txt.w1.b, w->txt.w3.b, ws.qkv_txt, nullptr, 0, 1, Mt, F, D};
   if (f8) {
-    LTRY(quant_inputs(ws.a_img, ws.a_txt, Mi, Mt, D, ws, st));
-    to_fp8(g, w->img.w1, w->txt.w1, &w->img.w3, &w->txt.w3, ws);
-    LTRY(gemm8(EPI_SWIGLU, g, st));
+    to_fp8(g, w->img.w1, w->txt.w1, &w->img.w3, &w->txt.w3, ws.q8_img, ws.s8_img, ws.q8_txt, ws.s8_txt);
+    g[0].C = ws.f8_img;
+    g[0].C_scale = ws.fs8_img;
+    g[1].C = ws.f8_txt;
+    g[1].C_scale = ws.fs8_txt;
+    LTRY(gemm8(EPI_SWIGLU_MX, g, st));
   } else {
     LTRY(gemm(LENS_KERNEL_GEMM, EPI_SWIGLU, bf, g, 2, st));
   }
@@ -375,8 +380,7 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   g[1] = GemmProblem{ws.qkv_txt, w->txt.w2.w, nullptr, w->txt.w2.b, nullptr, h_txt, mod_txt + 5 * D, D6, St > 0 ? St : 1,
                      Mt, D, F};
   if (f8) {
-    LTRY(quant_inputs(ws.qkv_img, ws.qkv_txt, Mi, Mt, F, ws, st));
-    to_fp8(g, w->img.w2, w->txt.w2, nullptr, nullptr, ws);
+    to_fp8(g, w->img.w2, w->txt.w2, nullptr, nullptr, ws.f8_img, ws.fs8_img, ws.f8_txt, ws.fs8_txt);
     LTRY(gemm8(EPI_GATED, g, st));
   } else {
     LTRY(gemm(LENS_KERNEL_GEMM, EPI_GATED, bf, g, 2, st));

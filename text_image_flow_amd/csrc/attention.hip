@@ -349,7 +349,36 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   const int p = q0 + ql;
-  if (p >= S) return;
+  if (p >= S) return;   // lanes l and l ^ 32 share p: pairs stay whole
+  if (a.O8_img) {
+    // MX fp8 output: the head's dims 0-31 (o[0]) and 32-63 (o[1]) are one
+    // block each, 16 values on this lane (dims 8 gg + 4 hl + e) and 16 on
+    // lane l ^ 32; after the swaps lanes 0-31 hold bytes 0-15 of a block
+    // and lanes 32-63 bytes 16-31
+    const int D = a.H * 64;
+    const bool img = p < a.S_img;
+    const int64_t row = img ? (int64_t)b * a.S_img + p : (int64_t)b * a.S_txt + (p - a.S_img);
+    unsigned char *q8 = (unsigned char *)(img ? a.O8_img : a.O8_txt) + row * D + h * 64;
+    unsigned char *sc = (unsigned char *)(img ? a.OS_img : a.OS_txt) + row * (D / 32) + h * 2;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float am = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) am = fmaxf(am, fabsf(o[t][k] * inv));
+      const auto sa = __builtin_amdgcn_permlane32_swap(__float_as_uint(am), __float_as_uint(am), false, false);
+      const int ex = mx_exponent(fmaxf(__uint_as_float(sa[0]), __uint_as_float(sa[1])));
+      unsigned d[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        d[gg] = mx_pack4(o[t][gg * 4] * inv, o[t][gg * 4 + 1] * inv, o[t][gg * 4 + 2] * inv, o[t][gg * 4 + 3] * inv,
+                         ex);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+      *(u32x4 *)(q8 + t * 32 + 16 * hl) = u32x4{s0[0], s0[1], s1[0], s1[1]};
+      if (hl == 0) sc[t] = (unsigned char)(ex + 127);
+    }
+    return;
+  }
   bf16 *dst = out_row<bf16>(a, b, p) + h * 64;
 #pragma unroll
   for (int gg = 0; gg < 4; ++gg) {

@@ -23,6 +23,50 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
+// ---------------------------------------------------------------- MX fp8
+// OCP MX fp8 (Lens-3.8B-4bit article, section 4: block-scaled low-precision
+// weights): e4m3 elements, one E8M0 power-of-two scale per 32 consecutive
+// elements.  Scale exponent of a block with largest magnitude amax: the
+// smallest e with amax <= 448 * 2^e, read off amax's fp32 bits (amax =
+// 1.f * 2^E: e = E - 8, plus one when f > 0.75), clamped to [-127, 127]; an
+// all-zero block takes -127.  The byte is e + 127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.f) return -127;
+  const unsigned b = __float_as_uint(amax);
+  const int ex = (int)(b >> 23) - 127 - 8 + ((b & 0x7fffff) > 0x600000 ? 1 : 0);
+  return ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+}
+
+// e4m3 code of y (|y| <= 448), round to nearest, ties to even; subnormals
+// below 2^-6 are multiples of 2^-9.
+__device__ __forceinline__ unsigned e4m3_code(float y) {
+  const unsigned u = __float_as_uint(y);
+  const unsigned sign = (u >> 24) & 0x80;
+  const float a = fabsf(y);
+  unsigned code;
+  if (a < 0.015625f) {
+    code = (unsigned)rintf(a * 512.0f);      // round-half-even
+  } else {
+    const unsigned au = u & 0x7fffffff;
+    int e = (int)(au >> 23) - 127;
+    unsigned m3 = (au >> 20) & 7, rest = au & 0xfffff;
+    if (rest > 0x80000 || (rest == 0x80000 && (m3 & 1))) ++m3;
+    if (m3 == 8) {
+      m3 = 0;
+      ++e;
+    }
+    code = ((unsigned)(e + 7) << 3) | m3;
+  }
+  return sign | code;
+}
+
+// Four elements of one block (scale exponent ex) as four e4m3 bytes, first
+// element in the low byte.
+__device__ __forceinline__ unsigned mx_pack4(float a, float b, float c, float d, int ex) {
+  return e4m3_code(ldexpf(a, -ex)) | (e4m3_code(ldexpf(b, -ex)) << 8) | (e4m3_code(ldexpf(c, -ex)) << 16) |
+         (e4m3_code(ldexpf(d, -ex)) << 24);
+}
+
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return hipSuccess or the launch error.
 
@@ -31,9 +75,11 @@ enum Epilogue {
   EPI_STORE_F32 = 1, // C = acc + bias                    (C float)
   EPI_GATED = 2,     // H += gate[m / rows_per_gate] * (acc + bias)   (H float)
   EPI_SWIGLU = 3,    // C = silu(acc1 + b1) * (acc3 + b3), B rows from w1 and w3
-  EPI_QKV = 4        // y = acc + bias split into per-head q | k | v (QkvOut; bf16 only):
+  EPI_QKV = 4,       // y = acc + bias split into per-head q | k | v (QkvOut; bf16 only):
                      // q, k RMS-normed with gain and rotated (RoPE), q scaled,
                      // all three written to the joint [B, H, S_pad, 64] layout
+  EPI_SWIGLU_MX = 5  // EPI_SWIGLU written as MX fp8: C e4m3 [M, N], C_scale E8M0 [M, N / 32]
+                     // (launch_gemm_fp8 only)
 };
 
 // One GEMM problem: C[M, N] = A[M, K] . W[N, K]^T (+ epilogue).
@@ -51,6 +97,7 @@ struct GemmProblem {
   // MX fp8 operands (launch_gemm_fp8 only): A, W, W3 hold e4m3 bytes and
   // these their E8M0 scales, one byte per 32 elements along K ([rows][K/32])
   const void *A_scale, *W_scale, *W3_scale;
+  void *C_scale;       // EPI_SWIGLU_MX: output scales
 };
 
 // Outputs of the QKV epilogue.  Problem 0 holds the image rows of the batch
@@ -111,6 +158,9 @@ struct AttnArgs {
   // bf16 path: the [64] q/k RMSNorm gains of both streams (q_img, k_img,
   // q_txt, k_txt), from which the kernel bounds every score; NULL: no bound
   const void *gain[4];
+  // bf16 path, optional: O also (or only) as MX fp8 rows (e4m3 [B*S, H*64],
+  // E8M0 [B*S, H*2]); with O8_img set, O_img / O_txt are not written
+  void *O8_img, *O8_txt, *OS_img, *OS_txt;
 };
 hipError_t launch_attention(const AttnArgs &a, bool bf16_path, hipStream_t stream);
 
@@ -122,9 +172,10 @@ struct NormModProblem {
   const float *shift, *scale;  // [B, D] rows, stride mod_stride
   int64_t mod_stride;
   int32_t rows, rows_per_sample;
+  void *out_scale;             // mx_out: E8M0 scales [rows, D / 32] (out: e4m3 [rows, D])
 };
 hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float eps, bool bf16_path,
-                                hipStream_t stream);
+                                hipStream_t stream, bool mx_out = false);
 
 // QK RMSNorm + RoPE + joint layout.  qkv_img [B*S_img, 3D], qkv_txt [B*S_txt, 3D].
 // q_scale multiplies q after RoPE (the bf16 attention kernel takes Q in

@@ -37,7 +37,7 @@ __device__ __forceinline__ void store4<bf16>(bf16 *dst, float a, float b, float 
 // NORM_RW rows per wave; D % 256 == 0 so each lane owns D/256 float4 groups of a row.
 constexpr int NORM_RW = 2;   // rows per wave of the norm kernel
 
-template <typename T, int G>
+template <typename T, int G, bool MX = false>
 __global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, NormModProblem p1, int split0,
                                                             float eps) {
   constexpr int D = G * 256;
@@ -80,12 +80,31 @@ __global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, N
     for (int i = 0; i < G; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
     ss = wave_sum(ss);
     const float rs = rsqrtf(ss / (float)D + eps);
-    T *out = (T *)p.out + (int64_t)r * D;
+    if constexpr (MX) {
+      // MX fp8 row: the 8 lanes of a 32-column block agree on its scale
+      // through three xor exchanges, each lane packs its 4 columns
+      unsigned *out = (unsigned *)((unsigned char *)p.out + (int64_t)r * D);
+      unsigned char *osc = (unsigned char *)p.out_scale + (int64_t)r * (D / 32);
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int c = (i * 64 + lane) * 4;
-      store4<T>(out + c, v[i].x * rs * (1.f + s4[i].x) + h4[i].x, v[i].y * rs * (1.f + s4[i].y) + h4[i].y,
-                v[i].z * rs * (1.f + s4[i].z) + h4[i].z, v[i].w * rs * (1.f + s4[i].w) + h4[i].w);
+      for (int i = 0; i < G; ++i) {
+        const float y0 = v[i].x * rs * (1.f + s4[i].x) + h4[i].x, y1 = v[i].y * rs * (1.f + s4[i].y) + h4[i].y;
+        const float y2 = v[i].z * rs * (1.f + s4[i].z) + h4[i].z, y3 = v[i].w * rs * (1.f + s4[i].w) + h4[i].w;
+        float am = fmaxf(fmaxf(fabsf(y0), fabsf(y1)), fmaxf(fabsf(y2), fabsf(y3)));
+        am = fmaxf(am, __shfl_xor(am, 1));
+        am = fmaxf(am, __shfl_xor(am, 2));
+        am = fmaxf(am, __shfl_xor(am, 4));
+        const int ex = mx_exponent(am);
+        out[i * 64 + lane] = mx_pack4(y0, y1, y2, y3, ex);
+        if ((lane & 7) == 0) osc[(i * 64 + lane) >> 3] = (unsigned char)(ex + 127);
+      }
+    } else {
+      T *out = (T *)p.out + (int64_t)r * D;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const int c = (i * 64 + lane) * 4;
+        store4<T>(out + c, v[i].x * rs * (1.f + s4[i].x) + h4[i].x, v[i].y * rs * (1.f + s4[i].y) + h4[i].y,
+                  v[i].z * rs * (1.f + s4[i].z) + h4[i].z, v[i].w * rs * (1.f + s4[i].w) + h4[i].w);
+      }
     }
     if (more) {
 #pragma unroll
@@ -537,33 +556,9 @@ __global__ __launch_bounds__(256) void flow_step_rescaled_kernel(float *x, const
 }
 
 // ------------------------------------------------ MX fp8 quantization
-// e4m3 code of y (|y| <= 448, finite), rounded to nearest, ties to even:
-// 3 mantissa bits on normals (exponents -6 .. 8), steps of 2^-9 below 2^-6.
-__device__ __forceinline__ unsigned e4m3_code(float y) {
-  const unsigned u = __float_as_uint(y);
-  const unsigned sign = (u >> 24) & 0x80;
-  const float a = fabsf(y);
-  unsigned code;
-  if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9 (8 = the smallest normal)
-    code = (unsigned)rintf(a * 512.0f);      // round-half-even
-  } else {
-    const unsigned au = u & 0x7fffffff;
-    int e = (int)(au >> 23) - 127;
-    unsigned m3 = (au >> 20) & 7, rest = au & 0xfffff;
-    if (rest > 0x80000 || (rest == 0x80000 && (m3 & 1))) ++m3;
-    if (m3 == 8) {
-      m3 = 0;
-      ++e;
-    }
-    code = ((unsigned)(e + 7) << 3) | m3;
-  }
-  return sign | code;
-}
-
 // One thread per 8 consecutive elements; the 4 threads of a 32-block are
-// consecutive lanes.  Scale exponent: the smallest e with amax <= 448 2^e,
-// read off amax's fp32 bits (amax = 1.f 2^E: e = E - 8, plus one when
-// f > 0.75), clamped to [-127, 127]; E8M0 byte = e + 127.
+// consecutive lanes (scale exponent and element codes: mx_exponent,
+// e4m3_code).
 template <typename T>
 __global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantProblem p0, MxQuantProblem p1, int cols) {
   const int64_t groups_per_row = cols / 8;
@@ -592,22 +587,9 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantProblem p0, MxQuan
   for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
-  int ex;
-  if (amax == 0.f) {
-    ex = -127;
-  } else {
-    const unsigned b = __float_as_uint(amax);
-    ex = (int)(b >> 23) - 127 - 8 + ((b & 0x7fffff) > 0x600000 ? 1 : 0);
-    ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
-  }
+  const int ex = mx_exponent(amax);
   if (!live) return;
-  unsigned lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const unsigned c = e4m3_code(ldexpf(v[e], -ex));
-    if (e < 4) lo |= c << (8 * e);
-    else hi |= c << (8 * (e - 4));
-  }
+  const unsigned lo = mx_pack4(v[0], v[1], v[2], v[3], ex), hi = mx_pack4(v[4], v[5], v[6], v[7], ex);
   *((uint2 *)p.q + gi) = make_uint2(lo, hi);
   if ((gi & 3) == 0) ((unsigned char *)p.scale)[gi >> 2] = (unsigned char)(ex + 127);
 }
@@ -630,7 +612,7 @@ hipError_t launch_mx_quant(const MxQuantProblem *p, int nprob, int cols, bool sr
 }
 
 hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float eps, bool bf16_path,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool mx_out) {
   NormModProblem p1 = nprob > 1 ? p[1] : NormModProblem{};
   if (nprob < 2) p1.rows = 0;
   const int rows = p[0].rows + p1.rows;
@@ -638,9 +620,12 @@ hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float
   const int split0 = (p[0].rows + NORM_RW - 1) / NORM_RW * NORM_RW;
   const int waves = split0 / NORM_RW + (p1.rows + NORM_RW - 1) / NORM_RW;
   dim3 grid((waves + 3) / 4);
+  if (mx_out && (!p[0].out_scale || (nprob > 1 && p1.rows > 0 && !p1.out_scale))) return hipErrorInvalidValue;
 #define NORM_CASE(g)                                                                                     \
   case g:                                                                                                \
-    if (bf16_path)                                                                                       \
+    if (mx_out)                                                                                          \
+      hipLaunchKernelGGL((norm_modulate_kernel<float, g, true>), grid, dim3(256), 0, stream, p[0], p1, split0, eps); \
+    else if (bf16_path)                                                                                  \
       hipLaunchKernelGGL((norm_modulate_kernel<bf16, g>), grid, dim3(256), 0, stream, p[0], p1, split0, eps);   \
     else                                                                                                 \
       hipLaunchKernelGGL((norm_modulate_kernel<float, g>), grid, dim3(256), 0, stream, p[0], p1, split0, eps);  \

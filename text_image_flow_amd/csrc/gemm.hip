@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
-  constexpr bool SWI = (EPI == EPI_SWIGLU);
+  constexpr bool SWI = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX);
   constexpr int OUTC = SWI ? BN / 2 : BN;
   constexpr int H = SWI ? NT / 2 : NT;          // output sub-tiles per wave along n
   static_assert(!SWI || NT % 2 == 0, "SwiGLU needs an even number of n tiles per wave");
@@ -598,7 +598,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
         unsigned bw[16], bw3[16];
         LOAD_BIAS16(bias, j, bw);
         if constexpr (SWI) LOAD_BIAS16(bias3, j, bw3);
-        if constexpr (EPI == EPI_STORE || EPI == EPI_SWIGLU) {
+        if constexpr (EPI == EPI_SWIGLU_MX) {
+          // one MX block = this (token, 32-feature group): 16 values here,
+          // 16 on the partner lane l ^ 32; after the swaps lanes 0-31 hold
+          // bytes 0-15 of the block and lanes 32-63 bytes 16-31
+          float b[4], b3[4], y[4][4], am = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            BIAS4(bw, j, q, b);
+            BIAS4(bw3, j, q, b3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              y[q][e] = silu_f(acc[i][j][4 * q + e] + b[e]) * (acc[i][j + H][4 * q + e] + b3[e]);
+              am = fmaxf(am, fabsf(y[q][e]));
+            }
+          }
+          const auto sa_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(am), __float_as_uint(am), false, false);
+          const int ex = mx_exponent(fmaxf(__uint_as_float(sa_[0]), __uint_as_float(sa_[1])));
+          unsigned d[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d[q] = mx_pack4(y[q][0], y[q][1], y[q][2], y[q][3], ex);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+          if (ok) {
+            const int64_t f = fw + j * 32;
+            *(u32x4 *)((unsigned char *)C + (int64_t)m * N + f + 16 * hl) = u32x4{s0[0], s0[1], s1[0], s1[1]};
+            if (hl == 0) ((unsigned char *)(sec ? p1.C_scale : p0.C_scale))[(int64_t)m * (N / 32) + f / 32] =
+                (unsigned char)(ex + 127);
+          }
+        } else if constexpr (EPI == EPI_STORE || EPI == EPI_SWIGLU) {
           unsigned pk[4][2];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -683,12 +711,14 @@ int cu_count() {
 // columns and K of the slab depth.
 template <int BM, int BN, int WM, int WN, int EPI, int GM = 4, bool BUF = false, bool F8 = false>
 hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st, const QkvOut *qo = nullptr, int max_grid = 0) {
-  const int outc = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  constexpr bool SWI = (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX);
+  const int outc = SWI ? BN / 2 : BN;
   if (np > 1 && (pr[0].N != pr[1].N || pr[0].K != pr[1].K)) return hipErrorInvalidValue;
   if (pr[0].N % outc || pr[0].K % (F8 ? 128 : gk::RBK) || pr[0].K <= 0) return hipErrorInvalidValue;
   if constexpr (F8) {
     for (int i = 0; i < np; ++i)
-      if (pr[i].M > 0 && (!pr[i].A_scale || !pr[i].W_scale || (EPI == EPI_SWIGLU && !pr[i].W3_scale)))
+      if (pr[i].M > 0 && (!pr[i].A_scale || !pr[i].W_scale || (SWI && !pr[i].W3_scale) ||
+                          (EPI == EPI_SWIGLU_MX && !pr[i].C_scale)))
         return hipErrorInvalidValue;
   }
   int ntm[2] = {0, 0}, tiles[2] = {0, 0};
@@ -816,7 +846,7 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st, const Qk
 // loads)
 template <int EPI>
 hipError_t dispatch_fp8(const GemmProblem *pr, int np, hipStream_t st, const QkvOut *qo) {
-  constexpr bool SWI = EPI == EPI_SWIGLU;
+  constexpr bool SWI = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX;
   const int outc = SWI ? 128 : 256;
   int tiles256 = 0;
   for (int i = 0; i < np; ++i) {
@@ -834,6 +864,7 @@ hipError_t launch_gemm_fp8(int epi, const GemmProblem *probs, int nprob, hipStre
     case EPI_STORE: return dispatch_fp8<EPI_STORE>(probs, nprob, stream, nullptr);
     case EPI_GATED: return dispatch_fp8<EPI_GATED>(probs, nprob, stream, nullptr);
     case EPI_SWIGLU: return dispatch_fp8<EPI_SWIGLU>(probs, nprob, stream, nullptr);
+    case EPI_SWIGLU_MX: return dispatch_fp8<EPI_SWIGLU_MX>(probs, nprob, stream, nullptr);
     case EPI_QKV: return dispatch_fp8<EPI_QKV>(probs, nprob, stream, qo);
   }
   return hipErrorInvalidValue;
