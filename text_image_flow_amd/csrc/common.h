@@ -37,34 +37,17 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return ex < -127 ? -127 : (ex > 127 ? 127 : ex);
 }
 
-// e4m3 code of y (|y| <= 448), round to nearest, ties to even; subnormals
-// below 2^-6 are multiples of 2^-9.
-__device__ __forceinline__ unsigned e4m3_code(float y) {
-  const unsigned u = __float_as_uint(y);
-  const unsigned sign = (u >> 24) & 0x80;
-  const float a = fabsf(y);
-  unsigned code;
-  if (a < 0.015625f) {
-    code = (unsigned)rintf(a * 512.0f);      // round-half-even
-  } else {
-    const unsigned au = u & 0x7fffffff;
-    int e = (int)(au >> 23) - 127;
-    unsigned m3 = (au >> 20) & 7, rest = au & 0xfffff;
-    if (rest > 0x80000 || (rest == 0x80000 && (m3 & 1))) ++m3;
-    if (m3 == 8) {
-      m3 = 0;
-      ++e;
-    }
-    code = ((unsigned)(e + 7) << 3) | m3;
-  }
-  return sign | code;
-}
-
 // Four elements of one block (scale exponent ex) as four e4m3 bytes, first
-// element in the low byte.
+// element in the low byte: x / 2^ex rounded to the nearest e4m3 value, ties
+// to even, subnormals in steps of 2^-9 (|x / 2^ex| <= 448 by the choice of
+// ex).  The gfx950 conversion v_cvt_pk_fp8_f32 does exactly this rounding:
+// checked on MI355X against an integer encoder of the rule on every fp32
+// bit pattern with magnitude in [2^-20, 448], both signs (smaller
+// magnitudes round to zero in both).
 __device__ __forceinline__ unsigned mx_pack4(float a, float b, float c, float d, int ex) {
-  return e4m3_code(ldexpf(a, -ex)) | (e4m3_code(ldexpf(b, -ex)) << 8) | (e4m3_code(ldexpf(c, -ex)) << 16) |
-         (e4m3_code(ldexpf(d, -ex)) << 24);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(a, -ex), ldexpf(b, -ex), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(c, -ex), ldexpf(d, -ex), w, true);
+  return (unsigned)w;
 }
 
 // ---------------------------------------------------------------- launchers

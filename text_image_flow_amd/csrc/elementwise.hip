@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void flow_step_rescaled_kernel(float *x, const
 // ------------------------------------------------ MX fp8 quantization
 // One thread per 8 consecutive elements; the 4 threads of a 32-block are
 // consecutive lanes (scale exponent and element codes: mx_exponent,
-// e4m3_code).
+// mx_pack4).
 template <typename T>
 __global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantProblem p0, MxQuantProblem p1, int cols) {
   const int64_t groups_per_row = cols / 8;
