@@ -82,16 +82,17 @@ def _rms(x):
 
 def _check_fp8_delta(name, g, r8, rx, h):
     """g: GPU fp8 result; r8: the oracle's fp8 block; rx: the exact block;
-    h: the block input.  The e4m3 rounding decisions of the GPU and of the
-    oracle differ wherever bf16 storage upstream (q, k, v, P, the norm and
-    attention outputs) moves an activation across a rounding boundary, so
+    h: the block input.  The kernels quantize each projection input from
+    its fp32 value, the oracle from its fp64 value; where the two differ by
+    more than the distance to an e4m3 rounding midpoint (fp32 arithmetic,
+    and the bf16 q, k, v and probabilities inside attention, upstream of
+    the quantization of its output) the codes differ by one step, so
     element-wise agreement is at the level of the quantization noise itself.
     The checks: (1) the GPU is as accurate as the ideal fp8 computation --
     its distance to the exact block at most 1.15x the oracle fp8 block's
     (measured 1.00x); (2) it is the same fp8 computation -- the RMS of its
-    difference to the oracle's fp8 block at most 0.06 x RMS(delta) (measured
-    0.038; emulating only the bf16 rounding at the quantization points on
-    the CPU gives 0.038 as well) and delta cosine >= 0.999."""
+    difference to the oracle's fp8 block at most 0.04 x RMS(delta) (measured
+    0.017-0.023 at 256 to 4096 image tokens) and delta cosine >= 0.999."""
     dg, d8, dx = (g - h).ravel(), (r8 - h).ravel(), (rx - h).ravel()
     e_gpu, e_ora = _rms(dg - dx), _rms(d8 - dx)
     rd = _rms(d8)
@@ -101,7 +102,7 @@ def _check_fp8_delta(name, g, r8, rx, h):
     print(msg, flush=True)
     assert np.all(np.isfinite(g)), name
     assert e_gpu <= 1.15 * e_ora, msg
-    assert _rms(dg - d8) <= 0.06 * rd and cos >= 0.999, msg
+    assert _rms(dg - d8) <= 0.04 * rd and cos >= 0.999, msg
 
 
 @pytest.mark.parametrize("case", [(1, 16, 16, 32, None), (2, 10, 13, 45, [45, 17])])
@@ -115,6 +116,16 @@ def test_block_fp8_parity(case):
     n = np.full(B, St) if tl is None else np.asarray(tl)
     pick = lambda a: np.concatenate([a[b, :n[b]] for b in range(B)])
     _check_fp8_delta("txt", pick(gt), pick(rt), pick(xt), pick(ht))
+
+
+def test_block_fp8_full_1024():
+    """One block at the full 1024^2 shape (4096 image + 512 text tokens, B = 1)."""
+    gi, gt, ri, rt, hi, ht = run_block_fp8(1, 64, 64, 512)
+    w = synth.block_weights(0, dtype="bf16")
+    h_img, h_txt, temb = synth.block_inputs(1, 4096, 512, dtype="bf16", seed=1)
+    xi, xt = O.block_forward(w, h_img, h_txt, temb, synth.image_positions(64, 64), synth.text_positions(512))
+    _check_fp8_delta("img", gi, ri, xi, hi)
+    _check_fp8_delta("txt", gt, rt, xt, ht)
 
 
 def test_dit_fp8_cosine_gate():
