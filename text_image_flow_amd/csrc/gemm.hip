@@ -277,13 +277,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
   // So when slab k is computed, W(k) is the newest W slab issued and at most
   // A(k+1) followed it (epilogue stores in between only make the wait
   // stricter).
-  int a_issued = 0, consumed = 0;
-  A_SETUP(at);
-  B_SETUP(bt);
-  ISSUE_A();
-  ISSUE_B();
-  ISSUE_A();
-
   const int frow = lane & 31, hl = lane >> 5;
   int a_row[MT], b_row[NT];
 #pragma unroll
@@ -296,6 +289,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
       b_row[j] = wn * WTN + j * 32 + frow;
     }
   }
+
+  // fp8 scales: per fragment row one dword = the 4 E8M0 bytes of a slab,
+  // loaded one slab ahead by raw buffer loads (a 32-bit row offset per
+  // fragment, the slab in the scalar offset).  SC_SETUP points the
+  // resources and offsets at tile t, SC_LOAD(koff) loads one slab's dwords
+  // (raw; the lane-half shift happens at use).
+  int so_a[F8 ? MT : 1], so_w[F8 ? NT : 1];
+  unsigned s_a[F8 ? MT : 1], s_w[F8 ? NT : 1], n_a[F8 ? MT : 1], n_w[F8 ? NT : 1];
+  __amdgpu_buffer_rsrc_t rs_a, rs_w, rs_w3;
+#define SC_SETUP(t_)                                                                                      \
+  do {                                                                                                    \
+    bool sec_;                                                                                            \
+    int m0_, n0_;                                                                                         \
+    tile_coords(t_, tiles0, ntm0, ntm1, ntn, GM, BM, OUTC, sec_, m0_, n0_);                               \
+    const GemmProblem &pp_ = sec_ ? p1 : p0;                                                              \
+    const int kb_ = K / 32;                                                                               \
+    rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)pp_.A_scale, (short)0, pp_.M * kb_, 0x00020000);     \
+    rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)pp_.W_scale, (short)0, pp_.N * kb_, 0x00020000);     \
+    rs_w3 = __builtin_amdgcn_make_buffer_rsrc((void *)(SWI ? pp_.W3_scale : pp_.W_scale), (short)0,       \
+                                              pp_.N * kb_, 0x00020000);                                   \
+    _Pragma("unroll") for (int i = 0; i < MT; ++i) so_a[i] = min(m0_ + a_row[i], pp_.M - 1) * kb_;        \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                      \
+      const bool third_ = SWI && b_row[j] >= BN / 2;                                                      \
+      so_w[j] = (n0_ + (third_ ? b_row[j] - BN / 2 : b_row[j])) * kb_;                                    \
+    }                                                                                                     \
+  } while (0)
+#define SC_LOAD(koff_)                                                                                    \
+  do {                                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < MT; ++i) n_a[i] =                                               \
+        (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rs_a, so_a[i], (koff_), 0);                        \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j) n_w[j] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32( \
+        SWI && b_row[j] >= BN / 2 ? rs_w3 : rs_w, so_w[j], (koff_), 0);                                   \
+  } while (0)
+
+  int a_issued = 0, consumed = 0;
+  A_SETUP(at);
+  B_SETUP(bt);
+  // the first tile's first scales go out before its first slabs, so that
+  // on every path the scale loads are followed by at least LDA A parts
+  if constexpr (F8) {
+    SC_SETUP(t_first);
+    SC_LOAD(0);
+  }
+  ISSUE_A();
+  ISSUE_B();
+  ISSUE_A();
   int ca = 0, cb = 0;                           // ring positions of the slab being computed
 
   for (int ct = t_first; ct < t_end; ct += nslot) {
@@ -305,59 +344,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
 
-    // fp8: this tile's scale rows (one dword = the 4 E8M0 bytes of a slab),
-    // the current slab's dwords and the next slab's, loaded one slab ahead
-    // (raw buffer loads: one 32-bit row offset per fragment, the slab in
-    // the scalar offset)
-    int so_a[F8 ? MT : 1], so_w[F8 ? NT : 1];
-    unsigned s_a[F8 ? MT : 1], s_w[F8 ? NT : 1], n_a[F8 ? MT : 1], n_w[F8 ? NT : 1];
-    __amdgpu_buffer_rsrc_t rs_a, rs_w, rs_w3;
-    if constexpr (F8) {
-      bool sec_;
-      int m0_, n0_;
-      tile_coords(ct, tiles0, ntm0, ntm1, ntn, GM, BM, OUTC, sec_, m0_, n0_);
-      const GemmProblem &pp = sec_ ? p1 : p0;
-      const int kb = K / 32;                    // scale bytes per row
-      rs_a = __builtin_amdgcn_make_buffer_rsrc((void *)pp.A_scale, (short)0, pp.M * kb, 0x00020000);
-      rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)pp.W_scale, (short)0, pp.N * kb, 0x00020000);
-      rs_w3 = __builtin_amdgcn_make_buffer_rsrc((void *)(SWI ? pp.W3_scale : pp.W_scale), (short)0, pp.N * kb,
-                                                0x00020000);
-#pragma unroll
-      for (int i = 0; i < MT; ++i) so_a[i] = min(m0_ + a_row[i], pp.M - 1) * kb;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const bool third = SWI && b_row[j] >= BN / 2;
-        so_w[j] = (n0_ + (third ? b_row[j] - BN / 2 : b_row[j])) * kb;
-      }
-      // lanes of the upper half take blocks 1 and 3 of a slab: shift them down
-#pragma unroll
-      for (int i = 0; i < MT; ++i) n_a[i] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rs_a, so_a[i], 0, 0) >> (8 * hl);
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-        n_w[j] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(SWI && b_row[j] >= BN / 2 ? rs_w3 : rs_w, so_w[j], 0, 0) >> (8 * hl);
-    }
-
     for (int kt = 0; kt < KT; ++kt) {
+      // fp8: the A parts are issued every slab (into a dead ring slot once
+      // the stream has ended), so the newest LDA loads are always A parts
+      if (F8 || a_issued > consumed + 1) wait_vm<LDA>();
+      else wait_vm<0>();
       if constexpr (F8) {
-        // this slab's scales (loaded during the previous slab), then the
-        // next slab's, issued before this iteration's W parts so that the
-        // slab wait at the top of the next iteration already covers them
+        // this slab's scales, loaded during the previous slab (raw dwords;
+        // lanes of the upper half take blocks 1 and 3: shift them down)
 #pragma unroll
-        for (int i = 0; i < MT; ++i) s_a[i] = n_a[i];
+        for (int i = 0; i < MT; ++i) {
+          s_a[i] = n_a[i] >> (8 * hl);
+          asm volatile("" : "+v"(s_a[i]));   // here, while the wait above covers the load
+        }
 #pragma unroll
-        for (int j = 0; j < NT; ++j) s_w[j] = n_w[j];
-        if (kt + 1 < KT) {
-#pragma unroll
-          for (int i = 0; i < MT; ++i)
-            n_a[i] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rs_a, so_a[i], (kt + 1) * 4, 0) >> (8 * hl);
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-            n_w[j] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32(SWI && b_row[j] >= BN / 2 ? rs_w3 : rs_w, so_w[j],
-                                                                    (kt + 1) * 4, 0) >> (8 * hl);
+        for (int j = 0; j < NT; ++j) {
+          s_w[j] = n_w[j] >> (8 * hl);
+          asm volatile("" : "+v"(s_w[j]));
         }
       }
-      if (a_issued > consumed + 1) wait_vm<LDA>();
-      else wait_vm<0>();
       // Barrier without a memory fence: the wait covers this wave's slab
       // loads, and every wave is done with the slots about to be refilled.
       wait_lgkm0();
@@ -399,11 +404,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
 #pragma unroll
               for (int i = ks * PB; i < (ks + 1) * PB; ++i) ISSUE_B_PART(i);
             }
-          } else {
-            if (do_a) {
-#pragma unroll
-              for (int i = (ks - KS / 2) * PA; i < (ks - KS / 2 + 1) * PA; ++i) ISSUE_A_PART(i);
+            // the next slab's scales (the next tile's first ones after the
+            // last slab; the last slab of the last tile reloads its own):
+            // after this slab's W parts and before its A parts, so the wait
+            // at the top of the next slab, which leaves only the newest A
+            // parts in flight, covers them a slab after they were issued
+            if (ks == 0) {
+              if (kt + 1 < KT) {
+                SC_LOAD((kt + 1) * 4);
+              } else if (ct + nslot < t_end) {
+                SC_SETUP(ct + nslot);
+                SC_LOAD(0);
+              } else {
+                SC_LOAD(kt * 4);
+              }
             }
+          } else {
+            // unconditional: once the A stream has ended (do_a false) these
+            // refill the slot of the next, nonexistent slab from the last
+            // tile's rows, which keeps the scale loads above followed by LDA
+            // loads on every path (the wait at the top of the next slab then
+            // leaves the A parts in flight without a compiler-inserted
+            // vmcnt(0) for the scales)
+#pragma unroll
+            for (int i = (ks - KS / 2) * PA; i < (ks - KS / 2 + 1) * PA; ++i) ISSUE_A_PART(i);
           }
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
@@ -682,6 +706,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
 #undef BIAS4
 #undef LOAD_BIAS16
   }
+  // fp8 leaves its last refills of dead ring slots in flight: they land
+  // before the workgroup's LDS is released
+  if constexpr (F8) wait_vm<0>();
+#undef SC_SETUP
+#undef SC_LOAD
 #undef ISSUE_A
 #undef ISSUE_B
 #undef ISSUE_A_PART
