@@ -56,6 +56,24 @@ def block_flops(d, S_img, S_txt, B, q_valid=None, kv_valid=None):
     return gemm, attn, adaln
 
 
+def sclk_mhz():
+    """Current shader clock from the amdgpu driver's pp_dpm_sclk (the line
+    marked '*'), or None where the file is not readable."""
+    import glob
+    import re
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            text = open(path).read()
+        except OSError:
+            continue
+        for line in text.splitlines():
+            if line.rstrip().endswith("*"):
+                m = re.search(r"(\d+)\s*[Mm]hz", line)
+                if m:
+                    return int(m.group(1))
+    return None
+
+
 def step_flops(d, S_img, S_txt, B):
     g, a, m = block_flops(d, S_img, S_txt, B)
     D = d.hidden
@@ -198,6 +216,48 @@ def main():
     fl = step_flops(d, S_IMG, S_TXT, B)
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
 
+    # ---- B = 1 forward (the cond half alone), same weights and shapes
+    fl1 = step_flops(d, S_IMG, S_TXT, 1)["total"]
+    for _ in range(args.warmup):
+        dv.dit_forward(cfg, dit, x_act[:1], feats[:1], t_tab[0][:1], ip, tp, None, v[:1], ws)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(args.steps):
+        dv.dit_forward(cfg, dit, x_act[:1], feats[:1], t_tab[k % LOOP_STEPS][:1], ip, tp, None, v[:1], ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_b1 = e0.elapsed_time(e1) / args.steps
+    b1 = {"ms": round(ms_b1, 3), "TFLOP/s": round(fl1 / (ms_b1 * 1e-3) / 1e12, 2),
+          "pct_of_bf16_peak": round(100 * fl1 / (ms_b1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2), "flops": fl1}
+
+    # ---- shader clock while the same steps run (sampled in a separate,
+    # untimed pass so the sampling thread cannot delay the timed launches)
+    clock = None
+    if sclk_mhz() is not None:
+        import threading
+        samples, done = [], threading.Event()
+
+        def sampler():
+            while not done.is_set():
+                c = sclk_mhz()
+                if c is not None:
+                    samples.append(c)
+                time.sleep(0.02)
+
+        th = threading.Thread(target=sampler, daemon=True)
+        th.start()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        done.set()
+        th.join()
+        if samples:
+            med = sorted(samples)[len(samples) // 2]
+            clock = {"sclk_mhz_median": med, "sclk_mhz_min": min(samples), "sclk_mhz_max": max(samples),
+                     "samples": len(samples), "source": "amdgpu pp_dpm_sclk current level, sampled every 20 ms "
+                                                        "during an untimed pass of the same steps",
+                     "pct_of_bf16_peak_at_measured_clock": round(100 * tflops / (PEAK_BF16_TFLOPS * med / 2400.0), 2)}
+
     # ---- second timed region: per-family kernel timing with HIP events
     kernels, roof = {}, None
     if not args.no_kernel_timer:
@@ -282,6 +342,7 @@ def main():
                    "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": fl["total"], "wall_s": round(wall, 3), "setup_s": round(setup_s, 1),
+        "b1_forward": b1, "clock": clock,
         "kernels": kernels, "roofline": roof, "cpu_baseline": cpu, "fp8_variant": fp8,
     }
     print(json.dumps(out))
