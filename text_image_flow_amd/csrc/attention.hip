@@ -11,19 +11,22 @@
 // same, so this order gives the same result as text-then-image.
 //
 // bf16 path (flash-style, one pass over K/V):
-//   * a wave owns 32 queries; four waves share 64-key K and V^T tiles that
+//   * a wave owns 32 queries; four waves share 64-key K and V tiles that
 //     direct global->LDS loads double-buffer in LDS;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane then holds one
 //     query (lane & 31) and 32 of the tile's 64 keys, so the row max needs
 //     one exchange with the partner lane (lane ^ 32) and the row sum none
 //     until the end;
 //   * P^T is rounded to bf16 in registers and used directly as the B operand
-//     of O^T += V^T P^T (V stored transposed, [64, S_pad]); O^T keeps one
-//     query per lane, so the online-softmax rescale is a per-lane scalar;
+//     of O^T += V^T P^T; V stays row-major ([S_pad, 64], like K) and
+//     ds_read_b64_tr_b16 assembles the transposed operand from it; O^T keeps
+//     one query per lane, so the online-softmax rescale is a per-lane scalar;
 //   * Q arrives pre-scaled by scale * log2(e), and the QK MFMAs start from
 //     -m, so p = exp2(s) with no subtraction; the running max is lazy and
 //     row sums add the bf16 probabilities with v_dot2;
-//   * the grid is flat and XCD-aware (one head's q-blocks share an L2).
+//   * the grid is flat and XCD-aware (one head's q-blocks share an L2);
+//   * O is written as bf16 rows, or (MX fp8 projections) as e4m3 rows with
+//     one E8M0 scale per 32 dims, quantized from fp32 in registers.
 // fp32 path: one thread per query, plain loops (correctness only).
 #include "common.h"
 
@@ -225,7 +228,7 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
 }
 
 __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
-  constexpr int TILE_BYTES = 64 * 128;        // K tile or V^T tile
+  constexpr int TILE_BYTES = 64 * 128;        // K tile or V tile (row-major)
   constexpr int STAGE = 2 * TILE_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 

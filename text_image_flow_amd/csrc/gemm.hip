@@ -33,6 +33,17 @@
 //    makes 8 consecutive bf16 per lane for a 16-byte store.  Biases arrive
 //    through scalar loads, which leave the vector-memory counter to the slabs.
 //
+// MX fp8 path (same kernel, F8 = true; the low-precision block projections
+// of the Lens-3.8B-4bit article, section 4, as OCP MX fp8): e4m3 operands
+// with one E8M0 scale per 32 along K, v_mfma_scale_f32_32x32x64_f8f6f4.
+//  * A slab is 128 k deep (still one 128-byte line per row), two MFMA k
+//    steps; each lane's scale dword holds its row's 4 block scales of the
+//    slab, loaded one slab ahead between the slab's W and A parts.
+//  * A fragments are read one row tile ahead, W fragments one k step ahead,
+//    and each MFMA is held in place by an empty asm on its accumulator.
+//  * EPI_SWIGLU_MX writes the SwiGLU output itself as MX fp8 (the input of
+//    the w2 projection).
+//
 // fp32 path: a plain LDS-tiled FMA kernel with the same epilogues, used by
 // the fp32 configuration (correctness, not speed).
 #include "common.h"
