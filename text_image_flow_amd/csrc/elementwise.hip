@@ -7,7 +7,11 @@
 //   * the skinny GEMM of AdaLN and the timestep MLP (time_text_embed);
 //   * timestep sinusoid; per-layer text-feature RMSNorm (txt_norm.0..3);
 //   * the CFG + Euler flow step (SOTA image-generation survey, "CFG" and
-//     "Rectified Flow"; the flow-matching path of the Lens paper summary).
+//     "Rectified Flow"; the flow-matching path of the Lens paper summary),
+//     plain or with the norm-rescaled combine (Lens blog, "Exploring Image
+//     Editing");
+//   * MX fp8 quantization (Lens-3.8B-4bit article, section 4), also fused
+//     into norm+modulate as an output format.
 // Statistics and arithmetic are float32; stores round to the storage type.
 #include "common.h"
 
