@@ -309,3 +309,30 @@ def test_sampler_turbo_free_running():
 
     ref = O.sample(vel, x0, 4)
     assert_parity(x.cpu().numpy(), ref, "x after 4 steps")
+
+
+def test_empty_inputs_touch_nothing():
+    """Zero tokens / rows: the entry points return LENS_OK and write nothing
+    (buffers around them keep a sentinel)."""
+    T, dv = _env()
+    from text_image_flow_amd import _lib as L
+    from text_image_flow_amd.device import ptr, stream_handle
+    x = torch.full((64, 128), 7.0, dtype=torch.float32, device="cuda")
+    v = torch.full((64, 128), 1.0, dtype=torch.float32, device="cuda")
+    lowp = torch.full((64, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    L.check(L.lens_flow_step(ptr(x), ptr(v), ptr(v), 0, 0.5, 5.0, ptr(lowp), L.LENS_BF16, stream_handle(None)))
+    L.check(L.lens_flow_step_rescaled(ptr(x), ptr(v), ptr(v), 0, 128, 0.5, 5.0, ptr(lowp), L.LENS_BF16,
+                                      stream_handle(None)))
+    q = torch.full((64, 128), 5, dtype=torch.uint8, device="cuda")
+    s = torch.full((64, 4), 9, dtype=torch.uint8, device="cuda")
+    L.check(L.lens_quantize_mxfp8(ptr(lowp), L.LENS_BF16, 0, 128, ptr(q), ptr(s), stream_handle(None)))
+    torch.cuda.synchronize()
+    assert bool((x == 7.0).all()) and bool((lowp.float() == 3.0).all())
+    assert bool((q == 5).all()) and bool((s == 9).all())
+    # empty tensors through the Python wrappers
+    e = torch.empty((0, 128), dtype=torch.float32, device="cuda")
+    dv.flow_step(e, e, e, 0.5, 5.0)
+    dv.flow_step_rescaled(e, e, e, 0.5, 5.0)
+    q0, s0 = dv.quantize_mxfp8(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert q0.shape == (0, 64) and s0.shape == (0, 2)
