@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timer", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the MX fp8 variant")
+    ap.add_argument("--no-b1", action="store_true",
+                    help="skip the B = 1 forward and the clock-sampling pass (profiles of the B = 2 step alone)")
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (counter calibration) and exit")
     args = ap.parse_args()
@@ -218,22 +220,23 @@ def main():
 
     # ---- B = 1 forward (the cond half alone), same weights and shapes
     fl1 = step_flops(d, S_IMG, S_TXT, 1)["total"]
-    for _ in range(args.warmup):
+    b1, clock = None, None
+    for _ in range(0 if args.no_b1 else args.warmup):
         dv.dit_forward(cfg, dit, x_act[:1], feats[:1], t_tab[0][:1], ip, tp, None, v[:1], ws)
     torch.cuda.synchronize()
-    e0.record(stream)
-    for k in range(args.steps):
-        dv.dit_forward(cfg, dit, x_act[:1], feats[:1], t_tab[k % LOOP_STEPS][:1], ip, tp, None, v[:1], ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_b1 = e0.elapsed_time(e1) / args.steps
-    b1 = {"ms": round(ms_b1, 3), "TFLOP/s": round(fl1 / (ms_b1 * 1e-3) / 1e12, 2),
-          "pct_of_bf16_peak": round(100 * fl1 / (ms_b1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2), "flops": fl1}
+    if not args.no_b1:
+        e0.record(stream)
+        for k in range(args.steps):
+            dv.dit_forward(cfg, dit, x_act[:1], feats[:1], t_tab[k % LOOP_STEPS][:1], ip, tp, None, v[:1], ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_b1 = e0.elapsed_time(e1) / args.steps
+        b1 = {"ms": round(ms_b1, 3), "TFLOP/s": round(fl1 / (ms_b1 * 1e-3) / 1e12, 2),
+              "pct_of_bf16_peak": round(100 * fl1 / (ms_b1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2), "flops": fl1}
 
     # ---- shader clock while the same steps run (sampled in a separate,
     # untimed pass so the sampling thread cannot delay the timed launches)
-    clock = None
-    if sclk_mhz() is not None:
+    if not args.no_b1 and sclk_mhz() is not None:
         import threading
         samples, done = [], threading.Event()
 
