@@ -334,6 +334,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
         SWI && b_row[j] >= BN / 2 ? rs_w3 : rs_w, so_w[j], (koff_), 0);                                   \
   } while (0)
 
+  // fp8 fragment reads: each lane's byte offset inside a ring slot, for the
+  // first row tile, per (k step, 16-byte half); the other row tiles sit a
+  // multiple of 16 rows further (same swizzle), i.e. at an immediate offset
+  int fa_off[F8 ? 2 * KS : 1], fb_off[F8 ? 2 * KS : 1];
+  if constexpr (F8) {
+#pragma unroll
+    for (int q = 0; q < 2 * KS; ++q) {
+      const int c = (q >> 1) * 4 + (q & 1) * 2 + hl;
+      fa_off[q] = a_row[0] * RROW + ((c ^ swz(a_row[0])) << 4);
+      fb_off[q] = b_row[0] * RROW + ((c ^ swz(b_row[0])) << 4);
+    }
+  }
+
   int a_issued = 0, consumed = 0;
   A_SETUP(at);
   B_SETUP(bt);
@@ -396,17 +409,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
         // live at once, which spills the 256-row tile).
         typedef int i32x8 __attribute__((ext_vector_type(8)));
         i32x8 fa8[2], fb8[2][NT];
-#define F8_FRAG(dst_, base_, row_, ks_)                                                                    \
+// fragment of the row tile drow_ rows past the first one (a multiple of 16)
+#define F8_FRAG(dst_, base_, off_, drow_, ks_)                                                             \
   do {                                                                                                     \
-    const int c0_ = (ks_) * 4 + hl, c1_ = (ks_) * 4 + 2 + hl;                                              \
-    const u32x4 lo_ = *(const u32x4 *)((base_) + (row_) * RROW + ((c0_ ^ swz(row_)) << 4));                 \
-    const u32x4 hi_ = *(const u32x4 *)((base_) + (row_) * RROW + ((c1_ ^ swz(row_)) << 4));                 \
+    const u32x4 lo_ = *(const u32x4 *)((base_) + (off_)[2 * (ks_)] + (drow_) * RROW);                      \
+    const u32x4 hi_ = *(const u32x4 *)((base_) + (off_)[2 * (ks_) + 1] + (drow_) * RROW);                  \
     dst_ = i32x8{(int)lo_[0], (int)lo_[1], (int)lo_[2], (int)lo_[3], (int)hi_[0], (int)hi_[1], (int)hi_[2], \
                  (int)hi_[3]};                                                                             \
   } while (0)
+        // b_row[j] - b_row[0] and a_row[i] - a_row[0], compile-time
+#define F8_BD(j_) (SWI ? ((j_) < H ? (j_) * 32 : BN / 2 + ((j_) - H) * 32) : (j_) * 32)
+#define F8_AD(i_) ((i_) * 32)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) F8_FRAG(fb8[0][j], sb, b_row[j], 0);
-        F8_FRAG(fa8[0], sa, a_row[0], 0);
+        for (int j = 0; j < NT; ++j) F8_FRAG(fb8[0][j], sb, fb_off, F8_BD(j), 0);
+        F8_FRAG(fa8[0], sa, fa_off, F8_AD(0), 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int cur = ks & 1;
@@ -442,11 +458,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
           }
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
-            if (i + 1 < MT) F8_FRAG(fa8[(i + 1) & 1], sa, a_row[i + 1], ks);
-            else if (ks + 1 < KS) F8_FRAG(fa8[0], sa, a_row[0], ks + 1);
+            if (i + 1 < MT) F8_FRAG(fa8[(i + 1) & 1], sa, fa_off, F8_AD(i + 1), ks);
+            else if (ks + 1 < KS) F8_FRAG(fa8[0], sa, fa_off, F8_AD(0), ks + 1);
             if (i == 0 && ks + 1 < KS) {
 #pragma unroll
-              for (int j = 0; j < NT; ++j) F8_FRAG(fb8[cur ^ 1][j], sb, b_row[j], ks + 1);
+              for (int j = 0; j < NT; ++j) F8_FRAG(fb8[cur ^ 1][j], sb, fb_off, F8_BD(j), ks + 1);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -462,6 +478,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
           }
         }
 #undef F8_FRAG
+#undef F8_BD
+#undef F8_AD
       } else {
       bf16x8 fa[2][MT], fb[2][NT];
 #define READ_FRAGS(buf_, ks_)                                                                              \
