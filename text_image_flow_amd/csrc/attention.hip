@@ -144,21 +144,24 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
   const int vlane = hl * 32 + ql;
   const int sw = (ql >> 1) & 7;   // rows ql and 32 + ql share the swizzle
+  // keys 0-31 (s0) fully before keys 32-63 (s1), so that in the bounded
+  // case the exponentials of s0 can go out while the s1 MFMAs still run
   f32x16 s0, s1;
   {
-    const int slot = (hl ^ sw) << 4;
-    const bf16x8 k0 = *(const bf16x8 *)(sKb + ql * 128 + slot);
-    const bf16x8 k1 = *(const bf16x8 *)(sKb + (32 + ql) * 128 + slot);
     const f32x16 c0 = (FIRST && !BOUNDED) ? f32x16{} : minit;
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], c0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[0], c0, 0, 0, 0);
+    s0 = c0;
+    s1 = c0;
   }
 #pragma unroll
-  for (int ks = 1; ks < 4; ++ks) {
+  for (int ks = 0; ks < 4; ++ks) {
     const int slot = ((ks * 2 + hl) ^ sw) << 4;
     const bf16x8 k0 = *(const bf16x8 *)(sKb + ql * 128 + slot);
-    const bf16x8 k1 = *(const bf16x8 *)(sKb + (32 + ql) * 128 + slot);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], s0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int slot = ((ks * 2 + hl) ^ sw) << 4;
+    const bf16x8 k1 = *(const bf16x8 *)(sKb + (32 + ql) * 128 + slot);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], s1, 0, 0, 0);
   }
   if constexpr (MASK) {
@@ -200,31 +203,31 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
     }
   }
   }
+  // probabilities of keys 0-31 (P^T k steps 0, 1), their PV MFMAs, then
+  // keys 32-63 (k steps 2, 3)
   bf16x8 pb[4];
   float lsum = l_run;   // the row sum continues the running sum directly
 #pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    bf16x2 p0 = {(bf16)__builtin_amdgcn_exp2f(s0[e]), (bf16)__builtin_amdgcn_exp2f(s0[e + 1])};
-    bf16x2 p1 = {(bf16)__builtin_amdgcn_exp2f(s0[8 + e]), (bf16)__builtin_amdgcn_exp2f(s0[9 + e])};
-    bf16x2 p2 = {(bf16)__builtin_amdgcn_exp2f(s1[e]), (bf16)__builtin_amdgcn_exp2f(s1[e + 1])};
-    bf16x2 p3 = {(bf16)__builtin_amdgcn_exp2f(s1[8 + e]), (bf16)__builtin_amdgcn_exp2f(s1[9 + e])};
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, lsum, false);
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, lsum, false);
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, lsum, false);
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(p3, ones, lsum, false);
-    pb[0][e] = p0[0]; pb[0][e + 1] = p0[1];
-    pb[1][e] = p1[0]; pb[1][e + 1] = p1[1];
-    pb[2][e] = p2[0]; pb[2][e + 1] = p2[1];
-    pb[3][e] = p3[0]; pb[3][e + 1] = p3[1];
+  for (int half = 0; half < 2; ++half) {
+    const f32x16 &sh = half ? s1 : s0;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      bf16x2 p0 = {(bf16)__builtin_amdgcn_exp2f(sh[e]), (bf16)__builtin_amdgcn_exp2f(sh[e + 1])};
+      bf16x2 p1 = {(bf16)__builtin_amdgcn_exp2f(sh[8 + e]), (bf16)__builtin_amdgcn_exp2f(sh[9 + e])};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, lsum, false);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, lsum, false);
+      pb[2 * half][e] = p0[0]; pb[2 * half][e + 1] = p0[1];
+      pb[2 * half + 1][e] = p1[0]; pb[2 * half + 1][e + 1] = p1[1];
+    }
+#pragma unroll
+    for (int ks = 2 * half; ks < 2 * half + 2; ++ks) {
+      const bf16x8 v0 = v_frag(sVb, ks, 0, vlane);
+      const bf16x8 v1 = v_frag(sVb, ks, 1, vlane);
+      o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb[ks], o[0], 0, 0, 0);
+      o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb[ks], o[1], 0, 0, 0);
+    }
   }
   l_run = lsum;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 v0 = v_frag(sVb, ks, 0, vlane);
-    const bf16x8 v1 = v_frag(sVb, ks, 1, vlane);
-    o[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb[ks], o[0], 0, 0, 0);
-    o[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb[ks], o[1], 0, 0, 0);
-  }
 }
 
 __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
