@@ -89,7 +89,8 @@ typedef struct {
 /* One Linear layer: w [out, in] in act_dtype, b [out] in act_dtype or NULL.
  * With cfg->gemm_fp8, the qkv, out, w1, w3 and w2 layers of every block
  * instead hold w as MX fp8: e4m3 bytes [out, in] with w_scale its E8M0
- * scales [out, in / 32] (lens_quantize_mxfp8 of the act_dtype weight); b
+ * scales in the LENS_MX_SLABS layout (lens_quantize_mxfp8 of the act_dtype
+ * weight with scale_layout LENS_MX_SLABS; in % 128 == 0); b
  * stays in act_dtype.  w_scale is ignored otherwise. */
 typedef struct {
   const void *w;
@@ -207,8 +208,14 @@ lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *
 /*
  * MX fp8 quantization of a row-major matrix along its rows: src [rows, cols]
  * (src_dtype LENS_BF16 or LENS_F32, cols a positive multiple of 32) ->
- * q_out [rows, cols] e4m3 bytes and scale_out [rows, cols / 32] E8M0 bytes
- * (value = 2^(byte - 127)).  Per block of 32 consecutive elements the scale
+ * q_out [rows, cols] e4m3 bytes and scale_out rows * cols / 32 E8M0 bytes
+ * (value = 2^(byte - 127)), one per block of 32 consecutive elements of a
+ * row; the scale of (row r, block j) sits at byte
+ *   LENS_MX_ROWS:  r * (cols / 32) + j
+ *   LENS_MX_SLABS: ((j / 4) * rows + r) * 4 + j % 4   (cols % 128 == 0)
+ * (slab-major: per 128-wide slab of a row its 4 scales form one 4-byte
+ * word, and the words of consecutive rows are adjacent; the layout the fp8
+ * GEMMs read, so w_scale of cfg->gemm_fp8 layers uses it).  Per block the scale
  * is the smallest power of two 2^e with max|x| <= 448 2^e (e clamped to
  * [-127, 127]; an all-zero block gets e = -127), and each element is
  * x / 2^e rounded to the nearest e4m3 value, ties to even.  This is the
@@ -218,8 +225,9 @@ lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *
  * bf16; here as MX fp8 rather than int4, the format the MI355X matrix cores
  * take directly).  Device pointers; rows >= 0.
  */
-lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t rows, int32_t cols, void *q_out,
-                                void *scale_out, void *hip_stream);
+enum { LENS_MX_ROWS = 0, LENS_MX_SLABS = 1 };
+lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t rows, int32_t cols,
+                                int32_t scale_layout, void *q_out, void *scale_out, void *hip_stream);
 
 /*
  * Opt-in kernel timer for measurement.  lens_timer_start(mask) makes every

@@ -151,11 +151,15 @@ def test_host_time_grid_matches_oracle():
 
 def test_fp8_argument_checks():
     Q = T.lens_quantize_mxfp8
-    assert Q(None, 1, -1, 64, None, None, None) == L.LENS_ERR_INVALID_ARG
-    assert Q(None, 1, 4, 48, None, None, None) == L.LENS_ERR_INVALID_ARG      # cols not a multiple of 32
-    assert Q(None, 7, 4, 64, None, None, None) == L.LENS_ERR_INVALID_ARG      # bad dtype
-    assert Q(None, 1, 4, 64, None, None, None) == L.LENS_ERR_INVALID_ARG      # NULL pointers
-    assert Q(None, 1, 0, 64, None, None, None) == L.LENS_OK                   # empty: nothing to do
+    R, S = T.LENS_MX_ROWS, T.LENS_MX_SLABS
+    assert Q(None, 1, -1, 64, R, None, None, None) == L.LENS_ERR_INVALID_ARG
+    assert Q(None, 1, 4, 48, R, None, None, None) == L.LENS_ERR_INVALID_ARG    # cols not a multiple of 32
+    assert Q(None, 1, 4, 64, S, None, None, None) == L.LENS_ERR_INVALID_ARG    # slabs: cols % 128
+    assert Q(None, 1, 4, 128, 2, None, None, None) == L.LENS_ERR_INVALID_ARG   # bad layout
+    assert Q(None, 7, 4, 64, R, None, None, None) == L.LENS_ERR_INVALID_ARG    # bad dtype
+    assert Q(None, 1, 4, 64, R, None, None, None) == L.LENS_ERR_INVALID_ARG    # NULL pointers
+    assert Q(None, 1, 0, 64, R, None, None, None) == L.LENS_OK                 # empty: nothing to do
+    assert Q(None, 1, 0, 256, S, None, None, None) == L.LENS_OK
     cfg = T.default_config(L.LENS_F32)
     assert cfg.gemm_fp8 == 0
     cfg.gemm_fp8 = 1                                                          # needs bf16 activations

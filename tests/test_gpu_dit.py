@@ -325,7 +325,8 @@ def test_empty_inputs_touch_nothing():
                                       stream_handle(None)))
     q = torch.full((64, 128), 5, dtype=torch.uint8, device="cuda")
     s = torch.full((64, 4), 9, dtype=torch.uint8, device="cuda")
-    L.check(L.lens_quantize_mxfp8(ptr(lowp), L.LENS_BF16, 0, 128, ptr(q), ptr(s), stream_handle(None)))
+    for layout in (L.LENS_MX_ROWS, L.LENS_MX_SLABS):
+        L.check(L.lens_quantize_mxfp8(ptr(lowp), L.LENS_BF16, 0, 128, layout, ptr(q), ptr(s), stream_handle(None)))
     torch.cuda.synchronize()
     assert bool((x == 7.0).all()) and bool((lowp.float() == 3.0).all())
     assert bool((q == 5).all()) and bool((s == 9).all())
@@ -333,6 +334,8 @@ def test_empty_inputs_touch_nothing():
     e = torch.empty((0, 128), dtype=torch.float32, device="cuda")
     dv.flow_step(e, e, e, 0.5, 5.0)
     dv.flow_step_rescaled(e, e, e, 0.5, 5.0)
-    q0, s0 = dv.quantize_mxfp8(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
+    q0, s0 = dv.quantize_mxfp8(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), layout=L.LENS_MX_ROWS)
+    q1, s1 = dv.quantize_mxfp8(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda"))
     torch.cuda.synchronize()
     assert q0.shape == (0, 64) and s0.shape == (0, 2)
+    assert q1.shape == (0, 256) and s1.shape == (2, 0, 4)

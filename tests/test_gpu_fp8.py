@@ -42,18 +42,27 @@ def _special_matrix(rows, cols, seed):
     return x
 
 
+@pytest.mark.parametrize("layout", ["rows", "slabs"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_mxfp8_quantize_bit_exact(dtype):
+def test_mxfp8_quantize_bit_exact(dtype, layout):
+    """Codes and scales bit for bit; the slab-major scales [cols / 128, rows,
+    4] are put back in row order ([rows, cols / 32]) for the comparison."""
+    import text_image_flow_amd as T
     dv = _dev()
-    x = _special_matrix(37, 160, 3)
+    cols = 160 if layout == "rows" else 384
+    x = _special_matrix(37, cols, 3)
     if dtype == "bf16":
         x = synth.bf16_round(x)
     d = dv.upload(x, 1 if dtype == "bf16" else 0)
-    q, s = dv.quantize_mxfp8(d)
+    q, s = dv.quantize_mxfp8(d, layout=T.LENS_MX_ROWS if layout == "rows" else T.LENS_MX_SLABS)
     torch.cuda.synchronize()
     qv, ev = O.mx_quantize(x)
+    s = s.cpu().numpy().astype(np.int64)
+    if layout == "slabs":
+        assert s.shape == (cols // 128, 37, 4)
+        s = s.transpose(1, 0, 2).reshape(37, cols // 32)
     np.testing.assert_array_equal(_decode_e4m3(q.cpu().numpy()), qv)
-    np.testing.assert_array_equal(s.cpu().numpy().astype(np.int64) - 127, ev)
+    np.testing.assert_array_equal(s - 127, ev)
 
 
 def run_block_fp8(B, gh, gw, St, txt_len=None, variant="canonical"):

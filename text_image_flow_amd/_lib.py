@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(_HERE, "liblens.so")
 
 LENS_OK, LENS_ERR_INVALID_ARG, LENS_ERR_UNSUPPORTED, LENS_ERR_WORKSPACE, LENS_ERR_HIP = 0, -1, -2, -3, -4
 LENS_F32, LENS_BF16 = 0, 1
+LENS_MX_ROWS, LENS_MX_SLABS = 0, 1
 LENS_KERNEL_GEMM, LENS_KERNEL_ATTENTION, LENS_KERNEL_NORM, LENS_KERNEL_QKNORM_ROPE, LENS_KERNEL_ADALN = range(5)
 LENS_KERNEL_COUNT = 5
 KERNEL_NAMES = ("gemm", "attention", "norm", "qknorm_rope", "adaln")
@@ -80,7 +81,7 @@ def lib() -> C.CDLL:
             "lens_dit_forward": (C.c_int, [cfgp, C.POINTER(LensDitW), P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]),
             "lens_flow_step": (C.c_int, [P, P, P, I64, F, F, P, C.c_int, P]),
             "lens_flow_step_rescaled": (C.c_int, [P, P, P, I64, I32, F, F, P, C.c_int, P]),
-            "lens_quantize_mxfp8": (C.c_int, [P, C.c_int, I64, I32, P, P, P]),
+            "lens_quantize_mxfp8": (C.c_int, [P, C.c_int, I64, I32, I32, P, P, P]),
             "lens_timer_start": (C.c_int, [C.c_uint32]),
             "lens_timer_stop": (C.c_int, [C.POINTER(D), C.POINTER(I64)]),
             "lens_status_string": (C.c_char_p, [C.c_int]),
@@ -148,8 +149,8 @@ def lens_flow_step_rescaled(x, v_cond, v_uncond, n_tokens, channels, dt, cfg_sca
                                          lowp_dtype, stream)
 
 
-def lens_quantize_mxfp8(src, src_dtype, rows, cols, q_out, scale_out, stream) -> int:
-    return lib().lens_quantize_mxfp8(src, src_dtype, rows, cols, q_out, scale_out, stream)
+def lens_quantize_mxfp8(src, src_dtype, rows, cols, scale_layout, q_out, scale_out, stream) -> int:
+    return lib().lens_quantize_mxfp8(src, src_dtype, rows, cols, scale_layout, q_out, scale_out, stream)
 
 
 def lens_timer_start(kind_mask: int) -> int:

@@ -596,17 +596,21 @@ lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *
   return LENS_OK;
 }
 
-lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t rows, int32_t cols, void *q_out,
-                                void *scale_out, void *hip_stream) {
+lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t rows, int32_t cols,
+                                int32_t scale_layout, void *q_out, void *scale_out, void *hip_stream) {
   if (src_dtype != LENS_F32 && src_dtype != LENS_BF16)
     return fail(LENS_ERR_INVALID_ARG, "src_dtype %d is not LENS_F32 or LENS_BF16", (int)src_dtype);
-  if (rows < 0 || cols <= 0 || cols % 32)
-    return fail(LENS_ERR_INVALID_ARG, "rows %lld / cols %d: need rows >= 0 and cols a positive multiple of 32",
-                (long long)rows, (int)cols);
+  if (scale_layout != LENS_MX_ROWS && scale_layout != LENS_MX_SLABS)
+    return fail(LENS_ERR_INVALID_ARG, "scale_layout %d is not LENS_MX_ROWS or LENS_MX_SLABS", (int)scale_layout);
+  const int unit = scale_layout == LENS_MX_SLABS ? 128 : 32;
+  if (rows < 0 || cols <= 0 || cols % unit)
+    return fail(LENS_ERR_INVALID_ARG, "rows %lld / cols %d: need rows >= 0 and cols a positive multiple of %d",
+                (long long)rows, (int)cols, unit);
   if (rows > 0 && (!src || !q_out || !scale_out)) return fail(LENS_ERR_INVALID_ARG, "NULL pointer");
   if (rows > (((int64_t)1 << 40) / cols)) return fail(LENS_ERR_UNSUPPORTED, "too many elements");
   MxQuantProblem q{src, q_out, scale_out, rows};
-  HIP_TRY(launch_mx_quant(&q, 1, cols, src_dtype == LENS_BF16, (hipStream_t)hip_stream));
+  HIP_TRY(launch_mx_quant(&q, 1, cols, src_dtype == LENS_BF16, scale_layout == LENS_MX_SLABS,
+                          (hipStream_t)hip_stream));
   return LENS_OK;
 }
 

@@ -365,7 +365,8 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
     const bool img = p < a.S_img;
     const int64_t row = img ? (int64_t)b * a.S_img + p : (int64_t)b * a.S_txt + (p - a.S_img);
     unsigned char *q8 = (unsigned char *)(img ? a.O8_img : a.O8_txt) + row * D + h * 64;
-    unsigned char *sc = (unsigned char *)(img ? a.OS_img : a.OS_txt) + row * (D / 32) + h * 2;
+    unsigned char *sc = (unsigned char *)(img ? a.OS_img : a.OS_txt);
+    const int64_t srows = (int64_t)a.B * (img ? a.S_img : a.S_txt);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float am = 0.f;
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
       const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
       const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
       *(u32x4 *)(q8 + t * 32 + 16 * hl) = u32x4{s0[0], s0[1], s1[0], s1[1]};
-      if (hl == 0) sc[t] = (unsigned char)(ex + 127);
+      if (hl == 0) sc[mx_scale_index(row, h * 2 + t, srows)] = (unsigned char)(ex + 127);
     }
     return;
   }

@@ -37,6 +37,13 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return ex < -127 ? -127 : (ex > 127 ? 127 : ex);
 }
 
+// Byte position of the scale of (row, 32-block kb) in the slab-major scale
+// layout the fp8 GEMM reads: [K / 128][rows][4], i.e. for every 128-wide
+// slab of the reduction axis each row's 4 block scales form one 4-byte word.
+__device__ __host__ __forceinline__ int64_t mx_scale_index(int64_t row, int64_t kb, int64_t rows) {
+  return ((kb >> 2) * rows + row) * 4 + (kb & 3);
+}
+
 // Four elements of one block (scale exponent ex) as four e4m3 bytes, first
 // element in the low byte: x / 2^ex rounded to the nearest e4m3 value, ties
 // to even, subnormals in steps of 2^-9 (|x / 2^ex| <= 448 by the choice of
@@ -61,8 +68,8 @@ enum Epilogue {
   EPI_QKV = 4,       // y = acc + bias split into per-head q | k | v (QkvOut; bf16 only):
                      // q, k RMS-normed with gain and rotated (RoPE), q scaled,
                      // all three written to the joint [B, H, S_pad, 64] layout
-  EPI_SWIGLU_MX = 5  // EPI_SWIGLU written as MX fp8: C e4m3 [M, N], C_scale E8M0 [M, N / 32]
-                     // (launch_gemm_fp8 only)
+  EPI_SWIGLU_MX = 5  // EPI_SWIGLU written as MX fp8: C e4m3 [M, N], C_scale E8M0 slab-major
+                     // (mx_scale_index; launch_gemm_fp8 only)
 };
 
 // One GEMM problem: C[M, N] = A[M, K] . W[N, K]^T (+ epilogue).
@@ -78,7 +85,8 @@ struct GemmProblem {
   int32_t rows_per_gate;
   int32_t M, N, K;
   // MX fp8 operands (launch_gemm_fp8 only): A, W, W3 hold e4m3 bytes and
-  // these their E8M0 scales, one byte per 32 elements along K ([rows][K/32])
+  // these their E8M0 scales, one byte per 32 elements along K, slab-major
+  // ([K / 128][rows][4], see mx_scale_index)
   const void *A_scale, *W_scale, *W3_scale;
   void *C_scale;       // EPI_SWIGLU_MX: output scales
 };
@@ -106,16 +114,18 @@ hipError_t launch_gemm_fp8(int epi, const GemmProblem *probs, int nprob, hipStre
                            const QkvOut *qo = nullptr);
 
 // MX fp8 quantization along rows: src [rows, cols] (bf16 or f32, cols % 32
-// == 0) -> q [rows, cols] e4m3 bytes and scales [rows, cols / 32] E8M0 bytes;
-// per block of 32 the tightest power-of-two scale that keeps every element
-// within +-448, elements rounded to nearest (ties to even).  Up to 2
-// problems in one launch (rows1 = 0 for one).
+// == 0) -> q [rows, cols] e4m3 bytes and E8M0 scales, one per 32 elements,
+// row-major [rows][cols / 32] or, with slabs (cols % 128 == 0), slab-major
+// (mx_scale_index); per block of 32 the tightest power-of-two scale that
+// keeps every element within +-448, elements rounded to nearest (ties to
+// even).  Up to 2 problems in one launch (rows1 = 0 for one).
 struct MxQuantProblem {
   const void *src;
   void *q, *scale;
   int64_t rows;
 };
-hipError_t launch_mx_quant(const MxQuantProblem *p, int nprob, int cols, bool src_bf16, hipStream_t stream);
+hipError_t launch_mx_quant(const MxQuantProblem *p, int nprob, int cols, bool src_bf16, bool slabs,
+                           hipStream_t stream);
 
 // RoPE table of the joint sequence: rope[j][i] = (cos, sin) of pos(j)[axis] *
 // theta^(-2 i' / axis_dim) for rotation pair i (pairs 0 .. axes0/2 - 1 on axis
@@ -141,8 +151,9 @@ struct AttnArgs {
   // bf16 path: the [64] q/k RMSNorm gains of both streams (q_img, k_img,
   // q_txt, k_txt), from which the kernel bounds every score; NULL: no bound
   const void *gain[4];
-  // bf16 path, optional: O also (or only) as MX fp8 rows (e4m3 [B*S, H*64],
-  // E8M0 [B*S, H*2]); with O8_img set, O_img / O_txt are not written
+  // bf16 path, optional: O as MX fp8 rows instead (e4m3 [B*S, H*64], E8M0
+  // scales slab-major over the B*S rows of each stream); with O8_img set,
+  // O_img / O_txt are not written
   void *O8_img, *O8_txt, *OS_img, *OS_txt;
 };
 hipError_t launch_attention(const AttnArgs &a, bool bf16_path, hipStream_t stream);
@@ -155,7 +166,7 @@ struct NormModProblem {
   const float *shift, *scale;  // [B, D] rows, stride mod_stride
   int64_t mod_stride;
   int32_t rows, rows_per_sample;
-  void *out_scale;             // mx_out: E8M0 scales [rows, D / 32] (out: e4m3 [rows, D])
+  void *out_scale;             // mx_out: E8M0 scales, slab-major over rows (out: e4m3 [rows, D])
 };
 hipError_t launch_norm_modulate(const NormModProblem *p, int nprob, int D, float eps, bool bf16_path,
                                 hipStream_t stream, bool mx_out = false);

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, N
       // MX fp8 row: the 8 lanes of a 32-column block agree on its scale
       // through three xor exchanges, each lane packs its 4 columns
       unsigned *out = (unsigned *)((unsigned char *)p.out + (int64_t)r * D);
-      unsigned char *osc = (unsigned char *)p.out_scale + (int64_t)r * (D / 32);
+      unsigned char *osc = (unsigned char *)p.out_scale;
 #pragma unroll
       for (int i = 0; i < G; ++i) {
         const float y0 = v[i].x * rs * (1.f + s4[i].x) + h4[i].x, y1 = v[i].y * rs * (1.f + s4[i].y) + h4[i].y;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, N
         am = fmaxf(am, __shfl_xor(am, 4));
         const int ex = mx_exponent(am);
         out[i * 64 + lane] = mx_pack4(y0, y1, y2, y3, ex);
-        if ((lane & 7) == 0) osc[(i * 64 + lane) >> 3] = (unsigned char)(ex + 127);
+        if ((lane & 7) == 0) osc[mx_scale_index(r, (i * 64 + lane) >> 3, rows)] = (unsigned char)(ex + 127);
       }
     } else {
       T *out = (T *)p.out + (int64_t)r * D;
@@ -562,9 +562,10 @@ __global__ __launch_bounds__(256) void flow_step_rescaled_kernel(float *x, const
 // ------------------------------------------------ MX fp8 quantization
 // One thread per 8 consecutive elements; the 4 threads of a 32-block are
 // consecutive lanes (scale exponent and element codes: mx_exponent,
-// mx_pack4).
+// mx_pack4).  Scales row-major ([rows][cols / 32]) or, with slabs,
+// slab-major (mx_scale_index).
 template <typename T>
-__global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantProblem p0, MxQuantProblem p1, int cols) {
+__global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantProblem p0, MxQuantProblem p1, int cols, bool slabs) {
   const int64_t groups_per_row = cols / 8;
   const int64_t g0 = p0.rows * groups_per_row;
   int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -595,13 +596,17 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantProblem p0, MxQuan
   if (!live) return;
   const unsigned lo = mx_pack4(v[0], v[1], v[2], v[3], ex), hi = mx_pack4(v[4], v[5], v[6], v[7], ex);
   *((uint2 *)p.q + gi) = make_uint2(lo, hi);
-  if ((gi & 3) == 0) ((unsigned char *)p.scale)[gi >> 2] = (unsigned char)(ex + 127);
+  if ((gi & 3) == 0) {
+    const int64_t r = gi / groups_per_row, kb = (gi - r * groups_per_row) >> 2;
+    ((unsigned char *)p.scale)[slabs ? mx_scale_index(r, kb, p.rows) : gi >> 2] = (unsigned char)(ex + 127);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_mx_quant(const MxQuantProblem *p, int nprob, int cols, bool src_bf16, hipStream_t stream) {
-  if (cols <= 0 || cols % 32) return hipErrorInvalidValue;
+hipError_t launch_mx_quant(const MxQuantProblem *p, int nprob, int cols, bool src_bf16, bool slabs,
+                           hipStream_t stream) {
+  if (cols <= 0 || cols % (slabs ? 128 : 32)) return hipErrorInvalidValue;
   MxQuantProblem p1 = nprob > 1 ? p[1] : MxQuantProblem{};
   if (nprob < 2) p1.rows = 0;
   const int64_t groups = (p[0].rows + p1.rows) * (cols / 8);
@@ -609,9 +614,9 @@ hipError_t launch_mx_quant(const MxQuantProblem *p, int nprob, int cols, bool sr
   const int64_t blocks = (groups + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (src_bf16)
-    hipLaunchKernelGGL(mx_quant_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, p[0], p1, cols);
+    hipLaunchKernelGGL(mx_quant_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, p[0], p1, cols, slabs);
   else
-    hipLaunchKernelGGL(mx_quant_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, p[0], p1, cols);
+    hipLaunchKernelGGL(mx_quant_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, p[0], p1, cols, slabs);
   return hipGetLastError();
 }
 

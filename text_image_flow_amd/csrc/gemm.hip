@@ -301,13 +301,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
     }
   }
 
-  // fp8 scales: per fragment row one dword = the 4 E8M0 bytes of a slab,
-  // loaded one slab ahead by raw buffer loads (a 32-bit row offset per
-  // fragment, the slab in the scalar offset).  SC_SETUP points the
-  // resources and offsets at tile t, SC_LOAD(koff) loads one slab's dwords
-  // (raw; the lane-half shift happens at use).
+  // fp8 scales, stored slab-major ([K / 128][rows][4] E8M0 bytes): per
+  // fragment row one dword = its 4 block scales of a slab, and the 32 rows of
+  // a row tile are 128 consecutive bytes, so one load instruction touches one
+  // cache line.  Loaded one slab ahead by raw buffer loads (a 32-bit row
+  // offset per fragment, slab * rows * 4 in the scalar offset).  SC_SETUP
+  // points the resources and offsets at tile t, SC_LOAD(slab) loads one
+  // slab's dwords (raw; the lane-half shift happens at use).
   int so_a[F8 ? MT : 1], so_w[F8 ? NT : 1];
   unsigned s_a[F8 ? MT : 1], s_w[F8 ? NT : 1], n_a[F8 ? MT : 1], n_w[F8 ? NT : 1];
+  int sa_step = 0, sw_step = 0;              // bytes per slab of the A / W scale arrays
   __amdgpu_buffer_rsrc_t rs_a, rs_w, rs_w3;
 #define SC_SETUP(t_)                                                                                      \
   do {                                                                                                    \
@@ -320,18 +323,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
     rs_w = __builtin_amdgcn_make_buffer_rsrc((void *)pp_.W_scale, (short)0, pp_.N * kb_, 0x00020000);     \
     rs_w3 = __builtin_amdgcn_make_buffer_rsrc((void *)(SWI ? pp_.W3_scale : pp_.W_scale), (short)0,       \
                                               pp_.N * kb_, 0x00020000);                                   \
-    _Pragma("unroll") for (int i = 0; i < MT; ++i) so_a[i] = min(m0_ + a_row[i], pp_.M - 1) * kb_;        \
+    sa_step = pp_.M * 4;                                                                                  \
+    sw_step = pp_.N * 4;                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < MT; ++i) so_a[i] = min(m0_ + a_row[i], pp_.M - 1) * 4;          \
     _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                      \
       const bool third_ = SWI && b_row[j] >= BN / 2;                                                      \
-      so_w[j] = (n0_ + (third_ ? b_row[j] - BN / 2 : b_row[j])) * kb_;                                    \
+      so_w[j] = (n0_ + (third_ ? b_row[j] - BN / 2 : b_row[j])) * 4;                                      \
     }                                                                                                     \
   } while (0)
-#define SC_LOAD(koff_)                                                                                    \
+#define SC_LOAD(slab_)                                                                                    \
   do {                                                                                                    \
+    const int ka_ = (slab_) * sa_step, kw_ = (slab_) * sw_step;                                           \
     _Pragma("unroll") for (int i = 0; i < MT; ++i) n_a[i] =                                               \
-        (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rs_a, so_a[i], (koff_), 0);                        \
+        (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rs_a, so_a[i], ka_, 0);                            \
     _Pragma("unroll") for (int j = 0; j < NT; ++j) n_w[j] = (unsigned)__builtin_amdgcn_raw_buffer_load_b32( \
-        SWI && b_row[j] >= BN / 2 ? rs_w3 : rs_w, so_w[j], (koff_), 0);                                   \
+        SWI && b_row[j] >= BN / 2 ? rs_w3 : rs_w, so_w[j], kw_, 0);                                       \
   } while (0)
 
   // fp8 fragment reads: each lane's byte offset inside a ring slot, for the
@@ -438,12 +444,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
             // parts in flight, covers them a slab after they were issued
             if (ks == 0) {
               if (kt + 1 < KT) {
-                SC_LOAD((kt + 1) * 4);
+                SC_LOAD(kt + 1);
               } else if (ct + nslot < t_end) {
                 SC_SETUP(ct + nslot);
                 SC_LOAD(0);
               } else {
-                SC_LOAD(kt * 4);
+                SC_LOAD(kt);
               }
             }
           } else {
@@ -676,7 +682,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16(GemmProblem p0, GemmPr
           if (ok) {
             const int64_t f = fw + j * 32;
             *(u32x4 *)((unsigned char *)C + (int64_t)m * N + f + 16 * hl) = u32x4{s0[0], s0[1], s1[0], s1[1]};
-            if (hl == 0) ((unsigned char *)(sec ? p1.C_scale : p0.C_scale))[(int64_t)m * (N / 32) + f / 32] =
+            if (hl == 0) ((unsigned char *)(sec ? p1.C_scale : p0.C_scale))[mx_scale_index(m, f / 32, M)] =
                 (unsigned char)(ex + 127);
           }
         } else if constexpr (EPI == EPI_STORE || EPI == EPI_SWIGLU) {

@@ -49,14 +49,17 @@ def stream_handle(stream=None) -> int:
 FP8_LINEARS = ("qkv", "out", "w1", "w3", "w2")   # the projections an MX fp8 model quantizes
 
 
-def quantize_mxfp8(w: torch.Tensor, stream=None):
+def quantize_mxfp8(w: torch.Tensor, stream=None, layout: int = L.LENS_MX_SLABS):
     """MX fp8 copy of a bf16 / f32 device matrix [rows, cols] (lens_quantize_mxfp8):
-    -> (e4m3 bytes [rows, cols] uint8, E8M0 scales [rows, cols / 32] uint8)."""
+    -> (e4m3 bytes [rows, cols] uint8, E8M0 scales uint8), the scales
+    [cols / 128, rows, 4] in the slab-major layout the fp8 GEMMs read
+    (LENS_MX_SLABS, the default) or [rows, cols / 32] (LENS_MX_ROWS)."""
     rows, cols = w.shape
     q = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
-    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=w.device)
+    shape = (cols // 128, rows, 4) if layout == L.LENS_MX_SLABS else (rows, cols // 32)
+    s = torch.empty(shape, dtype=torch.uint8, device=w.device)
     dt = L.LENS_BF16 if w.dtype == torch.bfloat16 else L.LENS_F32
-    L.check(L.lens_quantize_mxfp8(ptr(w), dt, rows, cols, ptr(q), ptr(s), stream_handle(stream)))
+    L.check(L.lens_quantize_mxfp8(ptr(w), dt, rows, cols, layout, ptr(q), ptr(s), stream_handle(stream)))
     return q, s
 
 
