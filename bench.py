@@ -180,7 +180,7 @@ def main():
     feats = dv.upload(np.concatenate([synth.text_features(1, S_TXT, d, seed=synth.SEED_TEXT_COND),
                                       synth.text_features(1, S_TXT, d, seed=synth.SEED_TEXT_UNCOND)]), T.LENS_BF16)
     ip, tp = dv.upload(synth.image_positions(*GRID)), dv.upload(synth.text_positions(S_TXT))
-    ts = dv.time_grid(LOOP_STEPS)
+    ts, dts = dv.time_grid(LOOP_STEPS)
     t_tab = dv.upload(np.repeat(ts[:, None], B, axis=1))
     v = torch.empty((B, S_IMG, d.out_ch), dtype=torch.float32, device="cuda")
     ws = dv.Workspace()
@@ -195,7 +195,7 @@ def main():
         k = k_state[0] % LOOP_STEPS
         k_state[0] += 1
         dv.dit_forward(model[0], model[1], x_act, feats, t_tab[k], ip, tp, None, v, ws)
-        dv.flow_step_rescaled(x, v[:1], v[1:], float(ts[k + 1] - ts[k]), CFG_SCALE, x_act[:1], T.LENS_BF16)
+        dv.flow_step_rescaled(x, v[:1], v[1:], float(dts[k]), CFG_SCALE, x_act[:1], T.LENS_BF16)
         x_act[1:].copy_(x_act[:1])
 
     for _ in range(args.warmup):

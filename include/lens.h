@@ -35,6 +35,9 @@
  *     workspace, sized by the *_workspace_bytes functions (256-byte aligned).
  *   - Matrices are row-major.  A Linear layer's weight is [out, in] (the
  *     input dimension contiguous) and its bias is [out] or NULL.
+ *   - Arguments and fields that name a lens_dtype or lens_status value are
+ *     declared int32_t, so that any integer a caller passes is checked (an
+ *     unknown value is LENS_ERR_INVALID_ARG) rather than read as an enum.
  *   - Activation / weight element type is cfg->act_dtype (LENS_BF16 or
  *     LENS_F32); residual streams, the timestep embedding, latents x (in the
  *     flow step) and the velocity v are always float32.  bf16 is stored as
@@ -76,7 +79,7 @@ typedef struct {
   float rope_theta;     /* 10000 */
   float eps;            /* 1e-6, all RMSNorms */
   float t_scale;        /* 1000: the sinusoid sees t_scale * t */
-  lens_dtype act_dtype; /* element type of weights and activations */
+  int32_t act_dtype;    /* a lens_dtype: element type of weights and activations */
   int32_t gemm_fp8;     /* 1: the block projections qkv, out, w1, w3, w2 run as
                            MX fp8 GEMMs (requires act_dtype LENS_BF16; see
                            lens_quantize_mxfp8): their inputs are quantized
@@ -124,7 +127,7 @@ typedef struct {
 } lens_dit_w;
 
 /* Fills *cfg with the Lens configuration and the given activation type. */
-void lens_default_config(lens_config *cfg, lens_dtype act_dtype);
+void lens_default_config(lens_config *cfg, int32_t act_dtype /* a lens_dtype */);
 
 /* Bytes of workspace lens_block_forward / lens_dit_forward need for batch B,
  * S_img image tokens and S_txt text tokens; 0 if the arguments are invalid. */
@@ -133,6 +136,13 @@ size_t lens_dit_workspace_bytes(const lens_config *cfg, int32_t B, int32_t S_img
 
 /*
  * One double-stream block, in place on the residual streams.
+ * Sources: the MMDiT block of the Lens paper summary (前置知识: each stream
+ * keeps its own weights and the two meet in one joint attention), the Lens
+ * blog's "Overview" (the AdaLN triple shift/scale/gate before attention and
+ * before the gated 1536x4096 MLP), and the Lens-Turbo-3.8B-bf16 article's
+ * "双流注意力机制", "自适应调制与 RMSNorm" and "3D RoPE" sections (per-stream
+ * qkv, per-head q/k RMSNorm with per-stream gains, RoPE axes [8, 28, 28]);
+ * padded text is masked per the blog's "Exploring Text Encoder".
  *   h_img [B, S_img, hidden] f32, h_txt [B, S_txt, hidden] f32: updated.
  *   temb  [B, hidden] f32: timestep embedding; AdaLN is computed inside as
  *         mod = W_mod . SiLU(temb) + b_mod for each stream.
@@ -156,6 +166,12 @@ lens_status lens_block_forward(const lens_config *cfg, const lens_block_w *w, fl
 
 /*
  * Whole denoiser: v = proj_out(norm_out(blocks(img_in(x), txt_in(f)), temb)).
+ * Sources: the Lens-Turbo-3.8B-bf16 article's architecture table and its
+ * "Patchify 补丁化与输出投影" (img_in on 2x2 patches of the 32-channel latent,
+ * norm_out.linear, proj_out), "多层级文本特征融合" (txt_norm.0..3 on four
+ * encoder layers, concatenated and projected by txt_in; also the Lens paper
+ * summary, 核心方法) and "自适应调制与 RMSNorm" (time_text_embed's timestep
+ * MLP); 48 blocks per the Lens blog's "Overview".
  *   x         [B, S_img, in_ch] act_dtype: patchified latent tokens (read only).
  *   txt_feats [B, S_txt, txt_layers * txt_feat_dim] act_dtype, layer-major.
  *   t         [B] f32 timesteps (device).
@@ -178,12 +194,17 @@ lens_status lens_dit_forward(const lens_config *cfg, const lens_dit_w *w, const 
 /*
  * Flow-matching Euler step with optional classifier-free guidance, on n
  * elements:  v = v_uncond + cfg_scale (v_cond - v_uncond)  (v = v_cond when
- * v_uncond is NULL);  x <- x + dt v.  x f32 is updated in place; v_cond and
+ * v_uncond is NULL);  x <- x + dt v.
+ * Sources: the SOTA image generation survey's "CFG" (the guided combination)
+ * and "Rectified Flow" (integrating the learned velocity with Euler steps),
+ * the Lens paper summary's 前置知识 (the straight path x_t = (1 - t) x0 +
+ * t x1 whose velocity the denoiser predicts; noise at t = 1), and the
+ * Lens-Turbo-3.8B-bf16 article (guidance 1.0: v_uncond NULL).  x f32 is updated in place; v_cond and
  * v_uncond are f32.  If x_lowp_out is not NULL it receives the new x in
  * lowp_dtype (the input of the next lens_dit_forward).  n >= 0.
  */
 lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond, int64_t n, float dt,
-                           float cfg_scale, void *x_lowp_out, lens_dtype lowp_dtype, void *hip_stream);
+                           float cfg_scale, void *x_lowp_out, int32_t lowp_dtype, void *hip_stream);
 
 /*
  * Flow-matching Euler step with norm-rescaled classifier-free guidance, on
@@ -203,10 +224,12 @@ lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond,
  */
 lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *v_uncond, int64_t n_tokens,
                                     int32_t channels, float dt, float cfg_scale, void *x_lowp_out,
-                                    lens_dtype lowp_dtype, void *hip_stream);
+                                    int32_t lowp_dtype, void *hip_stream);
 
 /*
- * MX fp8 quantization of a row-major matrix along its rows: src [rows, cols]
+ * MX-style fp8 quantization (e4m3 elements, one E8M0 scale per 32, with a
+ * non-saturating scale rule that differs from OCP MX v1.0's floor(log2 amax)
+ * - 8) of a row-major matrix along its rows: src [rows, cols]
  * (src_dtype LENS_BF16 or LENS_F32, cols a positive multiple of 32) ->
  * q_out [rows, cols] e4m3 bytes and scale_out rows * cols / 32 E8M0 bytes
  * (value = 2^(byte - 127)), one per block of 32 consecutive elements of a
@@ -226,7 +249,7 @@ lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *
  * take directly).  Device pointers; rows >= 0.
  */
 enum { LENS_MX_ROWS = 0, LENS_MX_SLABS = 1 };
-lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t rows, int32_t cols,
+lens_status lens_quantize_mxfp8(const void *src, int32_t src_dtype, int64_t rows, int32_t cols,
                                 int32_t scale_layout, void *q_out, void *scale_out, void *hip_stream);
 
 /*
@@ -236,8 +259,8 @@ lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t r
  * launched on.  lens_timer_stop(ms, launches) synchronises those events,
  * writes the summed kernel milliseconds and launch counts per family into
  * ms[LENS_KERNEL_COUNT] and launches[LENS_KERNEL_COUNT] (either may be
- * NULL), and switches the timer off.  Not thread-safe; meant for one
- * benchmark thread.
+ * NULL), and switches the timer off.  The timer state is per calling
+ * thread: start and stop on the thread that makes the timed calls.
  */
 typedef enum {
   LENS_KERNEL_GEMM = 0,        /* bf16 MFMA GEMM (all projections) */
@@ -250,7 +273,34 @@ typedef enum {
 lens_status lens_timer_start(uint32_t kind_mask);
 lens_status lens_timer_stop(double *ms, int64_t *launches);
 
-const char *lens_status_string(lens_status s);
+/*
+ * Sampling grid of the flow-matching Euler loop (HOST computation, host
+ * pointers).  t_out[k], k = 0..steps, and dt_out[k] = t_out[k + 1] -
+ * t_out[k], k < steps (either may be NULL), as float:
+ *   t_k = 1 - k / steps           (noise at t = 1, data at t = 0: the path
+ *                                  x_t = (1 - t) x0 + t x1 of the Lens paper
+ *                                  summary, 前置知识),
+ *   and with has_mu != 0 each point moved to e^mu t / (e^mu t + 1 - t), a
+ *   translation by mu in logit space that keeps t = 0 and t = 1 fixed.  The
+ *   same summary (前置知识, 方法步骤详情) trains on logit-normal timesteps
+ *   whose location mu grows linearly with the token count (mu = 1.06 for
+ *   the 512^2 stage); shifting the inference grid by that mu is the
+ *   reading taken here.  Computed in double, rounded once to float.
+ * Requires steps >= 1 and a finite mu; otherwise LENS_ERR_INVALID_ARG.
+ */
+lens_status lens_time_grid(int32_t steps, float mu, int32_t has_mu, float *t_out, float *dt_out);
+
+/*
+ * mu of the timestep shift at n_tokens image tokens, on the straight line
+ * through (n0, mu0) and (n1, mu1) (Lens paper summary, 方法步骤详情: mu is
+ * interpolated linearly in the token count; the pages give one point,
+ * mu = 1.06 at 512^2 = 1024 tokens, so the second is the caller's).
+ * HOST computation; *mu_out receives the value.  Requires n0 != n1, finite
+ * arguments and mu_out non-NULL; otherwise LENS_ERR_INVALID_ARG.
+ */
+lens_status lens_mu_for_tokens(int64_t n_tokens, double n0, double mu0, double n1, double mu1, double *mu_out);
+
+const char *lens_status_string(int32_t status /* a lens_status */);
 const char *lens_last_error(void);
 const char *lens_version(void);
 

@@ -44,6 +44,7 @@ def test_status_strings():
     for s, n in [(0, "LENS_OK"), (-1, "LENS_ERR_INVALID_ARG"), (-2, "LENS_ERR_UNSUPPORTED"),
                  (-3, "LENS_ERR_WORKSPACE"), (-4, "LENS_ERR_HIP")]:
         assert T.status_string(s) == n
+    assert T.status_string(42) == "unknown lens_status"
 
 
 def test_workspace_sizes():
@@ -135,18 +136,36 @@ def test_timer_argument_check():
     assert st == L.LENS_OK and n == [0] * 5 and ms == [0.0] * 5
 
 
-def test_host_time_grid_matches_oracle():
-    """The sampler's host-side grid (float32) against the oracle's fp64 grid,
-    uniform and shifted."""
+def test_time_grid_through_the_abi_matches_oracle():
+    """lens_time_grid (host code in the library) against the oracle's fp64
+    grid, uniform and shifted: t and dt = t[k + 1] - t[k] within one float
+    rounding, exact end points; lens_mu_for_tokens against the oracle's line."""
     import oracle as O
     from text_image_flow_amd import device as dv
     for steps in (1, 4, 20, 50):
-        for mu in (None, 0.0, 1.06, -0.5):
-            g = dv.time_grid(steps, mu)
-            assert g.dtype == np.float32
-            np.testing.assert_allclose(g, O.time_grid(steps, mu), rtol=0, atol=6e-8)
-            assert g[0] == 1.0 and g[-1] == 0.0
-    assert dv.mu_for_tokens(2560, 1024, 1.06, 4096, 1.5) == O.mu_for_tokens(2560, 1024, 1.06, 4096, 1.5)
+        for mu in (None, 0.0, 1.06, -0.5, 3.0):
+            t, dt = dv.time_grid(steps, mu)
+            assert t.dtype == np.float32 and t.shape == (steps + 1,) and dt.shape == (steps,)
+            ref = O.time_grid(steps, mu)
+            np.testing.assert_allclose(t, ref, rtol=0, atol=6e-8)
+            np.testing.assert_allclose(dt, np.diff(ref), rtol=0, atol=6e-8)
+            assert t[0] == 1.0 and t[-1] == 0.0 and np.all(dt < 0)
+    for n in (256, 1024, 2560, 4096, 8100):
+        assert abs(dv.mu_for_tokens(n, 1024, 1.06, 4096, 1.5) - O.mu_for_tokens(n, 1024, 1.06, 4096, 1.5)) < 1e-12
+
+
+def test_time_grid_argument_checks():
+    out = C.c_double()
+    t = np.zeros(8, np.float32)
+    assert T.lens_time_grid(0, 0.0, 0, t.ctypes.data, None) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_time_grid(-3, 0.0, 0, t.ctypes.data, None) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_time_grid(4, float("nan"), 1, t.ctypes.data, None) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_time_grid(4, float("nan"), 0, t.ctypes.data, None) == L.LENS_OK   # mu unused
+    assert T.lens_time_grid(4, 1.0, 1, None, None) == L.LENS_OK
+    assert T.lens_mu_for_tokens(10, 5.0, 1.0, 5.0, 2.0, C.byref(out)) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_mu_for_tokens(10, 5.0, 1.0, 6.0, 2.0, None) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_mu_for_tokens(10, 5.0, float("inf"), 6.0, 2.0, C.byref(out)) == L.LENS_ERR_INVALID_ARG
+    assert T.lens_mu_for_tokens(10, 5.0, 1.0, 6.0, 2.0, C.byref(out)) == L.LENS_OK and out.value == 6.0
 
 
 def test_fp8_argument_checks():

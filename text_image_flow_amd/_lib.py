@@ -8,7 +8,9 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblens.so")
+# LENS_LIBRARY names another build of the same library (the tests' host
+# sanitizer build); the default is the in-tree liblens.so
+LIB_PATH = os.environ.get("LENS_LIBRARY") or os.path.join(_HERE, "liblens.so")
 
 LENS_OK, LENS_ERR_INVALID_ARG, LENS_ERR_UNSUPPORTED, LENS_ERR_WORKSPACE, LENS_ERR_HIP = 0, -1, -2, -3, -4
 LENS_F32, LENS_BF16 = 0, 1
@@ -21,7 +23,7 @@ KERNEL_NAMES = ("gemm", "attention", "norm", "qknorm_rope", "adaln")
 EXPORTS = (
     "lens_default_config", "lens_block_workspace_bytes", "lens_dit_workspace_bytes", "lens_block_forward",
     "lens_dit_forward", "lens_flow_step", "lens_flow_step_rescaled", "lens_quantize_mxfp8", "lens_timer_start",
-    "lens_timer_stop",
+    "lens_timer_stop", "lens_time_grid", "lens_mu_for_tokens",
     "lens_status_string",
     "lens_last_error", "lens_version",
 )
@@ -84,6 +86,8 @@ def lib() -> C.CDLL:
             "lens_quantize_mxfp8": (C.c_int, [P, C.c_int, I64, I32, I32, P, P, P]),
             "lens_timer_start": (C.c_int, [C.c_uint32]),
             "lens_timer_stop": (C.c_int, [C.POINTER(D), C.POINTER(I64)]),
+            "lens_time_grid": (C.c_int, [I32, F, I32, P, P]),
+            "lens_mu_for_tokens": (C.c_int, [I64, D, D, D, D, C.POINTER(D)]),
             "lens_status_string": (C.c_char_p, [C.c_int]),
             "lens_last_error": (C.c_char_p, []),
             "lens_version": (C.c_char_p, []),
@@ -151,6 +155,15 @@ def lens_flow_step_rescaled(x, v_cond, v_uncond, n_tokens, channels, dt, cfg_sca
 
 def lens_quantize_mxfp8(src, src_dtype, rows, cols, scale_layout, q_out, scale_out, stream) -> int:
     return lib().lens_quantize_mxfp8(src, src_dtype, rows, cols, scale_layout, q_out, scale_out, stream)
+
+
+def lens_time_grid(steps, mu, has_mu, t_out, dt_out) -> int:
+    """t_out / dt_out: host addresses (or None) of steps + 1 / steps floats."""
+    return lib().lens_time_grid(steps, mu, has_mu, t_out, dt_out)
+
+
+def lens_mu_for_tokens(n_tokens, n0, mu0, n1, mu1, mu_out) -> int:
+    return lib().lens_mu_for_tokens(n_tokens, n0, mu0, n1, mu1, mu_out)
 
 
 def lens_timer_start(kind_mask: int) -> int:

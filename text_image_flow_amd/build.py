@@ -68,5 +68,38 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources (device code unchanged: every sanitizer flag applies to the host
+# pass only), for running the C-ABI argument tests on the CPU under the
+# sanitizers.  Load it with the ASan runtime preloaded (asan_runtime()).
+SAN_OUT = os.path.join(BUILD, "asan", "liblens_asan.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libasan", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the shared ASan runtime of the compiler that builds the library."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized() -> str:
+    d = os.path.dirname(SAN_OUT)
+    os.makedirs(d, exist_ok=True)
+    cc = hipcc()
+    objs, jobs = [], []
+    for s in SOURCES:
+        o = os.path.join(d, s.replace(".hip", ".o"))
+        objs.append(o)
+        jobs.append([cc, *FLAGS, *SAN_FLAGS, *EXTRA.get(s, []), "-c", os.path.join(CSRC, s), "-o", o])
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        list(ex.map(_run, jobs))
+    _run([cc, *FLAGS, *SAN_FLAGS, "-shared", *objs, "-o", SAN_OUT])
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

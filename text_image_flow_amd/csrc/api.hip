@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
+
 #include <string>
 #include <vector>
 
@@ -29,12 +31,16 @@ lens_status fail(lens_status s, const char *fmt, ...) {
 }
 
 // ------------------------------------------------------------ kernel timer
+// Per calling thread: a thread that starts the timer records and reads only
+// its own launches' events.  The events stay allocated for the thread's
+// lifetime (reused by the next start).
 struct Timer {
   uint32_t mask = 0;
   std::vector<hipEvent_t> pool;
   std::vector<int> kind_of;  // family of each recorded event pair
   size_t used = 0;
-} g_timer;
+};
+thread_local Timer g_timer;
 
 // Wraps one launch: records events around it when its family is timed.
 struct Timed {
@@ -422,7 +428,7 @@ lens_status adaln_all(const lens_config *c, const lens_block_w *const *blocks, i
 // ====================================================================== ABI
 extern "C" {
 
-void lens_default_config(lens_config *c, lens_dtype act) {
+void lens_default_config(lens_config *c, int32_t act) {
   if (!c) return;
   c->hidden = 1536;
   c->heads = 24;
@@ -572,7 +578,7 @@ lens_status lens_dit_forward(const lens_config *c, const lens_dit_w *w, const vo
 }
 
 lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond, int64_t n, float dt,
-                           float cfg_scale, void *x_lowp_out, lens_dtype lowp_dtype, void *hip_stream) {
+                           float cfg_scale, void *x_lowp_out, int32_t lowp_dtype, void *hip_stream) {
   if (n < 0) return fail(LENS_ERR_INVALID_ARG, "n = %lld < 0", (long long)n);
   if (n > 0 && (!x || !v_cond)) return fail(LENS_ERR_INVALID_ARG, "x and v_cond must not be NULL");
   if (x_lowp_out && lowp_dtype != LENS_F32 && lowp_dtype != LENS_BF16)
@@ -584,7 +590,7 @@ lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond,
 
 lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *v_uncond, int64_t n_tokens,
                                     int32_t channels, float dt, float cfg_scale, void *x_lowp_out,
-                                    lens_dtype lowp_dtype, void *hip_stream) {
+                                    int32_t lowp_dtype, void *hip_stream) {
   if (n_tokens < 0) return fail(LENS_ERR_INVALID_ARG, "n_tokens = %lld < 0", (long long)n_tokens);
   if (channels <= 0) return fail(LENS_ERR_INVALID_ARG, "channels = %d must be positive", (int)channels);
   if (n_tokens > 0 && (!x || !v_cond)) return fail(LENS_ERR_INVALID_ARG, "x and v_cond must not be NULL");
@@ -596,7 +602,7 @@ lens_status lens_flow_step_rescaled(float *x, const float *v_cond, const float *
   return LENS_OK;
 }
 
-lens_status lens_quantize_mxfp8(const void *src, lens_dtype src_dtype, int64_t rows, int32_t cols,
+lens_status lens_quantize_mxfp8(const void *src, int32_t src_dtype, int64_t rows, int32_t cols,
                                 int32_t scale_layout, void *q_out, void *scale_out, void *hip_stream) {
   if (src_dtype != LENS_F32 && src_dtype != LENS_BF16)
     return fail(LENS_ERR_INVALID_ARG, "src_dtype %d is not LENS_F32 or LENS_BF16", (int)src_dtype);
@@ -643,7 +649,34 @@ lens_status lens_timer_stop(double *ms, int64_t *launches) {
   return LENS_OK;
 }
 
-const char *lens_status_string(lens_status s) {
+lens_status lens_time_grid(int32_t steps, float mu, int32_t has_mu, float *t_out, float *dt_out) {
+  if (steps < 1) return fail(LENS_ERR_INVALID_ARG, "steps = %d: need at least one step", (int)steps);
+  if (has_mu && !std::isfinite(mu)) return fail(LENS_ERR_INVALID_ARG, "mu is not finite");
+  // t_k = 1 - k / steps, optionally moved by mu in logit space:
+  // t' = e^mu t / (e^mu t + 1 - t), which keeps 0 and 1 fixed
+  const double e = has_mu ? std::exp((double)mu) : 1.0;
+  auto point = [&](int k) {
+    const double t = 1.0 - (double)k / steps;
+    return has_mu ? e * t / (e * t + 1.0 - t) : t;
+  };
+  for (int k = 0; k <= steps; ++k) {
+    const double t = point(k);
+    if (t_out) t_out[k] = (float)t;
+    if (dt_out && k < steps) dt_out[k] = (float)(point(k + 1) - t);
+  }
+  return LENS_OK;
+}
+
+lens_status lens_mu_for_tokens(int64_t n_tokens, double n0, double mu0, double n1, double mu1, double *mu_out) {
+  if (!mu_out) return fail(LENS_ERR_INVALID_ARG, "mu_out is NULL");
+  if (!std::isfinite(n0) || !std::isfinite(n1) || !std::isfinite(mu0) || !std::isfinite(mu1))
+    return fail(LENS_ERR_INVALID_ARG, "line points must be finite");
+  if (n0 == n1) return fail(LENS_ERR_INVALID_ARG, "the line needs two distinct token counts (n0 == n1 = %g)", n0);
+  *mu_out = mu0 + ((double)n_tokens - n0) * (mu1 - mu0) / (n1 - n0);
+  return LENS_OK;
+}
+
+const char *lens_status_string(int32_t s) {
   switch (s) {
     case LENS_OK: return "LENS_OK";
     case LENS_ERR_INVALID_ARG: return "LENS_ERR_INVALID_ARG";

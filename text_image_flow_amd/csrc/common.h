@@ -24,9 +24,12 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
 // ---------------------------------------------------------------- MX fp8
-// OCP MX fp8 (Lens-3.8B-4bit article, section 4: block-scaled low-precision
-// weights): e4m3 elements, one E8M0 power-of-two scale per 32 consecutive
-// elements.  Scale exponent of a block with largest magnitude amax: the
+// MX-style fp8 with a non-saturating scale (the block-scaled low-precision
+// weights of the Lens-3.8B-4bit article, section 4): e4m3 elements, one E8M0
+// power-of-two scale per 32 consecutive elements.  Unlike the OCP MX v1.0
+// rule (scale exponent floor(log2 amax) - 8, saturating the few elements
+// that then exceed 448), the scale here is the tightest one under which no
+// element saturates.  Scale exponent of a block with largest magnitude amax: the
 // smallest e with amax <= 448 * 2^e, read off amax's fp32 bits (amax =
 // 1.f * 2^E: e = E - 8, plus one when f > 0.75), clamped to [-127, 127]; an
 // all-zero block takes -127.  The byte is e + 127.

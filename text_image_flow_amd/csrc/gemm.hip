@@ -34,7 +34,8 @@
 //    through scalar loads, which leave the vector-memory counter to the slabs.
 //
 // MX fp8 path (same kernel, F8 = true; the low-precision block projections
-// of the Lens-3.8B-4bit article, section 4, as OCP MX fp8): e4m3 operands
+// of the Lens-3.8B-4bit article, section 4, as MX-style fp8 with a
+// non-saturating scale): e4m3 operands
 // with one E8M0 scale per 32 along K, v_mfma_scale_f32_32x32x64_f8f6f4.
 //  * A slab is 128 k deep (still one 128-byte line per row), two MFMA k
 //    steps; each lane's scale dword holds its row's 4 block scales of the

@@ -188,22 +188,22 @@ def flow_step_rescaled(x, v_cond, v_uncond, dt, cfg_scale, x_lowp=None, lowp_dty
                                       float(cfg_scale), ptr(x_lowp), lowp_dtype, stream_handle(stream)))
 
 
-def time_grid(steps: int, mu: float | None = None) -> np.ndarray:
-    """t_k = 1 - k/N, k = 0..N (noise at t = 1), as float32.  With mu, each
-    point moves to e^mu t / (e^mu t + 1 - t) (a shift by mu in logit space,
-    end points fixed): the resolution-dependent schedule of the Lens paper
-    summary (前置知识 and 方法步骤详情: mu(n) linear in the token count,
-    mu = 1.06 at 512^2)."""
-    t = 1.0 - np.arange(steps + 1, dtype=np.float64) / steps
-    if mu is not None:
-        e = float(np.exp(mu))
-        t = e * t / (e * t + 1.0 - t)
-    return t.astype(np.float32)
+def time_grid(steps: int, mu: float | None = None):
+    """(t, dt) of the sampling loop from lens_time_grid: t [steps + 1] and
+    dt [steps] float32 host arrays (uniform grid from t = 1 to 0, or moved
+    by mu in logit space)."""
+    t = np.empty(steps + 1, np.float32)
+    dt = np.empty(max(steps, 0), np.float32)
+    L.check(L.lens_time_grid(int(steps), float(mu if mu is not None else 0.0), int(mu is not None),
+                             t.ctypes.data, dt.ctypes.data))
+    return t, dt
 
 
 def mu_for_tokens(n: int, n0: float, mu0: float, n1: float, mu1: float) -> float:
-    """mu on the line through (n0, mu0) and (n1, mu1), at token count n."""
-    return mu0 + (float(n) - n0) * (mu1 - mu0) / (n1 - n0)
+    """mu on the line through (n0, mu0) and (n1, mu1) at n tokens (lens_mu_for_tokens)."""
+    out = C.c_double()
+    L.check(L.lens_mu_for_tokens(int(n), float(n0), float(mu0), float(n1), float(mu1), C.byref(out)))
+    return out.value
 
 
 class Sampler:
@@ -235,7 +235,7 @@ class Sampler:
         """x: [n, S_img, in_ch] float32 latent tokens, updated in place;
         x_act0: the same values in the activation type (the first DiT input).
         txt_feats: [B, S_txt, F] act type (cond rows first); txt_len [B] or None."""
-        ts = time_grid(steps, self.mu)
+        ts, dts = time_grid(steps, self.mu)
         t_tab = upload(np.repeat(ts[:, None], self.B, axis=1), None, self.device)   # [steps+1, B]
         # first input, duplicated for the uncond half (plain copies)
         for h in range(self.B // self.n):
@@ -248,7 +248,7 @@ class Sampler:
             vc = self.v[:self.n]
             vu = self.v[self.n:] if self.use_cfg else None
             step = flow_step_rescaled if self.norm_rescale else flow_step
-            step(x, vc, vu, float(ts[k + 1] - ts[k]), self.cfg_scale, self.x_act[:self.n], self.cfg.act_dtype)
+            step(x, vc, vu, float(dts[k]), self.cfg_scale, self.x_act[:self.n], self.cfg.act_dtype)
             if self.use_cfg:
                 self.x_act[self.n:].copy_(self.x_act[:self.n])
         return x
