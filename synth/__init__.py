@@ -126,12 +126,20 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def _draw(kind: str, shape, g: np.random.Generator, variant: str) -> np.ndarray:
+# 'late' variant: base of the q / k RMSNorm gains per (stream, tensor)
+_LATE_GAINS = {("img", "q_gain"): 2.0, ("txt", "q_gain"): 2.0, ("img", "k_gain"): 0.5, ("txt", "k_gain"): 2.5}
+
+
+def _draw(kind: str, shape, g: np.random.Generator, variant: str, stream: str = "", name: str = "") -> np.ndarray:
     """One weight tensor.  'canonical': linear weights and biases N(0, 0.02),
     norm gains 1 + N(0, 0.02).  'wide': the same weights, but gains U(0.5, 1.5)
     and biases N(0, 1), so gain and bias paths carry visible signal.
     'sharp': canonical, but norm gains 2.05 + N(0, 0.02): q.k logits about 4x
-    larger, so attention is sharp and its running max moves often."""
+    larger, so attention is sharp and its running max moves often.
+    'late': canonical, but q gains 2, image k gains 0.5 and text k gains 2.5
+    (+ N(0, 0.02)): keys of the text stream score far above image keys, so
+    a softmax pass that meets the image keys first (in key order) sees its
+    running maximum jump when it reaches the text keys."""
     if kind == "w":
         return g.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
     if kind == "b":
@@ -140,7 +148,10 @@ def _draw(kind: str, shape, g: np.random.Generator, variant: str) -> np.ndarray:
     if kind == "g":
         if variant == "wide":
             return g.uniform(0.5, 1.5, size=shape).astype(np.float32)
-        base = np.float32(2.05) if variant == "sharp" else np.float32(1.0)
+        if variant == "late" and (stream, name) in _LATE_GAINS:
+            base = np.float32(_LATE_GAINS[(stream, name)])
+        else:
+            base = np.float32(2.05) if variant == "sharp" else np.float32(1.0)
         return base + g.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
     raise ValueError(kind)
 
@@ -161,9 +172,15 @@ def block_weights(block: int, d: Dims = LENS, dtype: str = "bf16", seed: int = S
         ws = {}
         for ti, (name, kind, shape) in enumerate(_STREAM_TENSORS):
             g = rng(seed, block, 100 * si + ti)
-            ws[name] = _store(_draw(kind, shape(d), g, variant), dtype)
+            ws[name] = _store(_draw(kind, shape(d), g, variant, s, name), dtype)
         out[s] = ws
     return out
+
+
+def without_biases(w: dict) -> dict:
+    """The same block weights with every Linear bias removed (None): the
+    bias-free Linear layers a checkpoint may carry."""
+    return {s: {k: (None if k.endswith("_b") else v) for k, v in ws.items()} for s, ws in w.items()}
 
 
 def top_weights(d: Dims = LENS, dtype: str = "bf16", seed: int = SEED_WEIGHTS,

@@ -5,17 +5,24 @@ import numpy as np
 
 COS_MIN = 0.9995
 MAXABS_REL = 2e-2
-# Block deltas (h_out - h_in) are a stricter, extra check.  With bf16 GEMM
-# inputs, rounding the modulated activations alone gives max|err| up to ~0.03
-# x RMS(delta) against exact fp64 (emulated on the CPU at the storage points
-# the kernels use), so deltas are held to 5e-2 x RMS and the same cosine.
+# Block deltas (h_out - h_in) are a stricter, extra check, held to bars
+# derived from tests/rounding_model.py: the oracle block with bf16 rounding
+# at every point where the kernels store bf16 (tests/test_parity_budget.py
+# recomputes these budgets and checks each bar is at least 1.25x its own).
+# Canonical and 'wide' weights: max|err| up to 0.030 x RMS(delta) (0.037
+# without biases), so deltas are held to 5e-2 x RMS and the same cosine;
+# 'wide' outputs (block update several times h) inherit that bar (budget
+# 0.026 x RMS(out)).
 DELTA_REL = 5e-2
 # Sharp attention (q/k RMSNorm gains near 2, logits ~4x the canonical ones):
 # the error of a logit from the bf16 rounding of q and k grows with the
-# logit, and the same CPU emulation gives max|err| ~0.043 x RMS(delta) for
-# the sharp test case (0.034 from rounding q and k alone, against 0.003 with
-# gains <= 1.5), so sharp cases are held to 8e-2.
+# logit; budget 0.060 x RMS(delta) on the ragged sharp case, 0.051 at 1024^2.
 SHARP_DELTA_REL = 8e-2
+# 'late' gains (text keys scoring far above image keys, so the softmax's
+# running max jumps late in the key pass): budget 0.073 x RMS(delta) and
+# 0.028 x RMS(out) at the 1024^2 block.
+LATE_DELTA_REL = 1e-1
+LATE_OUT_REL = 4e-2
 
 
 def stats(gpu, ref):

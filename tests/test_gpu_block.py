@@ -6,7 +6,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.parity import DELTA_REL, SHARP_DELTA_REL, assert_parity
+from tests.parity import DELTA_REL, LATE_DELTA_REL, LATE_OUT_REL, SHARP_DELTA_REL, assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -19,14 +19,17 @@ def _dev():
     return dv
 
 
-def run_case(dtype, B, gh, gw, St, txt_len=None, variant="canonical", block=0, seed_h=1):
+def run_case(dtype, B, gh, gw, St, txt_len=None, variant="canonical", block=0, seed_h=1, biases=True):
     dv = _dev()
     import text_image_flow_amd as T
     act = T.LENS_BF16 if dtype == "bf16" else T.LENS_F32
     cfg = T.default_config(act)
     Si = gh * gw
-    print(f"case dtype={dtype} B={B} grid={gh}x{gw} S_txt={St} txt_len={txt_len} variant={variant}", flush=True)
+    print(f"case dtype={dtype} B={B} grid={gh}x{gw} S_txt={St} txt_len={txt_len} variant={variant} "
+          f"biases={biases}", flush=True)
     w = synth.block_weights(block, dtype=dtype, variant=variant)
+    if not biases:
+        w = synth.without_biases(w)
     h_img, h_txt, temb = synth.block_inputs(B, Si, St, dtype=dtype, seed=seed_h)
     ip, tp = synth.image_positions(gh, gw), synth.text_positions(St)
 
@@ -52,6 +55,8 @@ def run_case(dtype, B, gh, gw, St, txt_len=None, variant="canonical", block=0, s
     orel = DELTA_REL if (dtype == "bf16" and variant in ("wide", "sharp")) else 2e-2
     if dtype == "bf16" and variant == "sharp":
         drel = orel = SHARP_DELTA_REL
+    if dtype == "bf16" and variant == "late":
+        drel, orel = LATE_DELTA_REL, LATE_OUT_REL
     assert_parity(gi, ri, "h_img", rel=orel)
     assert_parity(gi - h_img, ri - h_img, "delta_img", rel=drel)
     vt = np.concatenate([gt[b, :tl[b]] for b in range(B)]) if St else np.zeros((0, cfg.hidden))
@@ -100,3 +105,106 @@ def test_block_bf16_two_tiles_exact():
 def test_block_bf16_config1_full():
     """bf16, 64x64 image grid (4096 tokens, 1024^2) + 512 text tokens, B = 1."""
     run_case("bf16", 1, 64, 64, 512)
+
+
+def test_block_bf16_without_biases():
+    """Every Linear without a bias (NULL bias pointers): the bias-free paths
+    of the QKV epilogue (norm, gain, RoPE), the gated residual and SwiGLU
+    epilogues, and the AdaLN GEMV."""
+    run_case("bf16", 2, 10, 13, 45, txt_len=[45, 17], biases=False)
+
+
+def test_block_f32_without_biases():
+    run_case("f32", 2, 9, 11, 13, txt_len=[13, 5], biases=False)
+
+
+def test_block_bf16_late_max_jump_full_1024():
+    """1024^2 (4096 image + 512 text tokens, 72 key tiles of 64) with q gains
+    2, image k gains 0.5 and text k gains 2.5: the score bound from the
+    gains (about 62 in log2 units) exceeds the fixed-offset limit, so the
+    attention takes its online running max, and the text keys, which come
+    after all image keys in the kernel's key order, score far above them
+    (the running max jumps by more than the lazy-rescale threshold for most
+    queries, checked on the oracle's q and k in tests/test_parity_budget.py),
+    so the deferred rescale of the accumulated output runs on late tiles."""
+    run_case("bf16", 1, 64, 64, 512, variant="late")
+
+
+def test_block_bf16_late_max_jump_masked():
+    """The same gains on ragged, masked shapes (two samples, text lengths
+    45 and 17: the jump comes from the valid text keys only)."""
+    run_case("bf16", 2, 10, 13, 45, txt_len=[45, 17], variant="late")
+
+
+def test_block_bf16_sharp_full_1024():
+    """Gains near 2.05 everywhere (online running max over 72 key tiles)."""
+    run_case("bf16", 1, 64, 64, 512, variant="sharp")
+
+
+# ------------------------------------------------------------ robustness
+def _block_setup(B=2, gh=10, gw=13, St=45, txt_len=(45, 17)):
+    dv = _dev()
+    import text_image_flow_amd as T
+    cfg = T.default_config(T.LENS_BF16)
+    w = synth.block_weights(0)
+    h_img, h_txt, temb = synth.block_inputs(B, gh * gw, St)
+    ip, tp = synth.image_positions(gh, gw), synth.text_positions(St)
+    blk = dv.DeviceBlock(w, T.LENS_BF16)
+    args = (dv.upload(temb), dv.upload(ip), dv.upload(tp), dv.upload(np.asarray(txt_len, np.int32)))
+    return dv, cfg, blk, h_img, h_txt, args
+
+
+def test_block_nan_poisoned_workspace_gives_identical_output():
+    """The workspace is scratch: filled with NaN bytes before the call, the
+    block's outputs are bit-identical to a run on a zeroed workspace (every
+    intermediate is written before it is read)."""
+    dv, cfg, blk, h_img, h_txt, args = _block_setup()
+    outs = []
+    for fill in (0, 255):
+        ws = dv.Workspace()
+        buf = ws.get(dv.L.lens_block_workspace_bytes(cfg, 2, 130, 45))
+        buf.fill_(fill)
+        hi, ht = dv.upload(h_img), dv.upload(h_txt)
+        dv.block_forward(cfg, blk, hi, ht, *args, ws)
+        torch.cuda.synchronize()
+        outs.append((hi.cpu().numpy(), ht.cpu().numpy()))
+    assert np.all(np.isfinite(outs[0][0]))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1][0], outs[1][1][0])
+    assert np.array_equal(outs[0][1][1, :17], outs[1][1][1, :17])   # valid text rows of sample 1
+
+
+def test_block_writes_nothing_outside_its_outputs():
+    """h_img / h_txt placed inside larger buffers whose leading and trailing
+    rows hold a canary: after the call the canaries are intact."""
+    dv, cfg, blk, h_img, h_txt, args = _block_setup()
+    pad, canary = 37, np.float32(-1234.5)
+    bufs = []
+    for h in (h_img, h_txt):
+        B, S, D = h.shape
+        big = torch.full((B * S + 2 * pad, D), float(canary), dtype=torch.float32, device="cuda")
+        big[pad:pad + B * S] = torch.from_numpy(h.reshape(B * S, D)).cuda()
+        bufs.append((big, big[pad:pad + B * S].view(B, S, D)))
+    dv.block_forward(cfg, blk, bufs[0][1], bufs[1][1], *args, dv.Workspace())
+    torch.cuda.synchronize()
+    for big, _ in bufs:
+        b = big.cpu().numpy()
+        assert np.all(b[:pad] == canary) and np.all(b[-pad:] == canary)
+    assert np.all(np.isfinite(bufs[0][1].cpu().numpy()))
+
+
+def test_block_nan_propagates_within_its_sample_only():
+    """A NaN in one image token of sample 0 reaches every output of sample 0
+    (its key enters every softmax row of the sample) and nothing of sample
+    1, which stays bit-identical to a clean run: a NaN is never masked."""
+    dv, cfg, blk, h_img, h_txt, args = _block_setup()
+    clean = (dv.upload(h_img), dv.upload(h_txt))
+    dv.block_forward(cfg, blk, *clean, *args, dv.Workspace())
+    bad = h_img.copy()
+    bad[0, 5, 7] = np.nan
+    poisoned = (dv.upload(bad), dv.upload(h_txt))
+    dv.block_forward(cfg, blk, *poisoned, *args, dv.Workspace())
+    torch.cuda.synchronize()
+    ci, ct = (t.cpu().numpy() for t in clean)
+    pi, pt = (t.cpu().numpy() for t in poisoned)
+    assert np.all(np.isnan(pi[0])) and np.all(np.isnan(pt[0]))
+    assert np.array_equal(pi[1], ci[1]) and np.array_equal(pt[1, :17], ct[1, :17])

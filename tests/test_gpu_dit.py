@@ -1,20 +1,26 @@
 """GPU parity of lens_dit_forward, lens_flow_step and the sampler loop
 against the fp64 oracle on the same seeded inputs.
 
-Whole-model parity runs where the oracle finishes in seconds: two blocks at
-small token counts, and one block at the real 1024^2 / 1440^2 / 2:1 and 1:2
-shapes (embeddings, a block and the final layer all at full size).  The full
-48-block model at 1024^2 with the cond/uncond batch of 2 (the benchmarked
-launch) is checked through properties that hold at any size: finite output,
-bit-identical reruns, and exact sample-swap symmetry (batch independence);
-its MX fp8 variant by the same properties and its cosine to the bf16
-model."""
+Whole-model parity: two blocks at small token counts; one block at the real
+1024^2 / 1440^2 / 2:1 and 1:2 shapes (embeddings, a block and the final
+layer all at full size); the full 48-block model's v at 1024^2 (B = 1)
+against the oracle's 48-block forward (about two minutes of fp64 on the
+host); and, teacher-forced, blocks 0, 23 and 47 of the 48-block model at the
+benchmarked cond + uncond launch (1024^2, B = 2), at 1440^2 (B = 1) and at
+2:1 and 1:2 with batch 8 and masked text: the GPU chains lens_block_forward
+through all 48 blocks from the oracle's embeddings, and the oracle runs each
+sampled block from the GPU's own input to it, so block outputs and block
+deltas are compared at the model's own modulation scale.  The 48-block
+model at the benchmarked launch is also checked through properties that
+hold at any size: bit-identical reruns and exact sample-swap symmetry
+(batch independence); its MX fp8 variant by the same properties, its cosine
+to the bf16 model and, at B = 1, to the oracle's exact v."""
 import numpy as np
 import pytest
 
 import oracle as O
 import synth
-from tests.parity import assert_parity
+from tests.parity import DELTA_REL, MAXABS_REL, assert_parity
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -120,6 +126,38 @@ def test_dit_one_block_aspect_masked_batch8(gh, gw):
     check_dit(1, "bf16", 8, gh, gw, 512, txt_len=tl, t=[0.8] * 8)
 
 
+def lazy_blocks(n, variant="canonical", ahead=6, threads=8):
+    """Weights of blocks 0 .. n-1 in order, generated on a thread pool a few
+    blocks ahead of their use (the oracle holds one block at a time)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(threads) as ex:
+        futs = {i: ex.submit(synth.block_weights, i, variant=variant) for i in range(min(ahead, n))}
+        for i in range(n):
+            if i + ahead < n:
+                futs[i + ahead] = ex.submit(synth.block_weights, i + ahead, variant=variant)
+            yield futs.pop(i).result()
+
+
+class _Progress(dict):
+    """capture= target of oracle.dit_forward that prints a line per block
+    (the 48-block oracle pass is long) and keeps nothing."""
+
+    def __setitem__(self, i, value):
+        print(f"  oracle block {i} done", flush=True)
+
+
+@pytest.fixture(scope="module")
+def full_inputs_b1():
+    """Inputs of the 1024^2 B = 1 forward and the oracle's 48-block v for them."""
+    import time
+    x, feats, t, ip, tp = make_inputs(1, 64, 64, 512, "bf16", t=[0.6])
+    t0 = time.time()
+    print("oracle: 48-block forward at 1024^2, B = 1", flush=True)
+    ref = O.dit_forward(synth.top_weights(), lazy_blocks(48), x, feats, t, ip, tp, capture=_Progress())
+    print(f"oracle: done in {time.time() - t0:.1f} s", flush=True)
+    return x, feats, t, ip, tp, ref
+
+
 @pytest.fixture(scope="module")
 def full_dit():
     """The 48-block bf16 model at the benchmarked shapes, uploaded once for
@@ -165,14 +203,139 @@ def test_dit_full_48_blocks_1024_properties(full_dit):
     _full_run_props(T.default_config(T.LENS_BF16), full_dit)
 
 
+def _run_b1(cfg, dit, x, feats, t, ip, tp):
+    T, dv = _env()
+    v = torch.empty((1, x.shape[1], 128), dtype=torch.float32, device="cuda")
+    dv.dit_forward(cfg, dit, dv.upload(x, T.LENS_BF16), dv.upload(feats, T.LENS_BF16), dv.upload(t), dv.upload(ip),
+                   dv.upload(tp), None, v, dv.Workspace())
+    torch.cuda.synchronize()
+    return v.cpu().numpy()
+
+
+@pytest.mark.timeout(1200)
+def test_dit_full_48_blocks_1024_b1_against_oracle(full_dit, full_inputs_b1):
+    """v of the whole 48-block bf16 denoiser at 1024^2 (4096 image + 512 text
+    tokens, B = 1) against the oracle's 48-block fp64 forward on the same
+    inputs, at the parity bar."""
+    T, dv = _env()
+    x, feats, t, ip, tp, ref = full_inputs_b1
+    print("dit 48 blocks bf16 1024^2 B=1 vs oracle", flush=True)
+    v = _run_b1(T.default_config(T.LENS_BF16), full_dit, x, feats, t, ip, tp)
+    assert_parity(v, ref, "v (48 blocks, 1024^2, B = 1)")
+
+
+@pytest.mark.timeout(1200)
+def test_dit_fp8_full_48_blocks_1024_b1_cosine_gate(full_dit, full_inputs_b1):
+    """The MX fp8 variant of the same forward against the oracle's exact v:
+    the pages' low-precision gate, cosine >= 0.9976 (Lens-3.8B-4bit article,
+    section 4: a single quantized DiT pass against the unquantized one)."""
+    T, dv = _env()
+    x, feats, t, ip, tp, ref = full_inputs_b1
+    dit8 = dv.DeviceDit(synth.top_weights(), [dv.DeviceBlock.fp8_copy(b) for b in full_dit.blocks], T.LENS_BF16)
+    cfg8 = T.default_config(T.LENS_BF16)
+    cfg8.gemm_fp8 = 1
+    v = _run_b1(cfg8, dit8, x, feats, t, ip, tp).ravel().astype(np.float64)
+    r = ref.ravel()
+    cos = float(v @ r / np.linalg.norm(v) / np.linalg.norm(r))
+    print(f"v cosine, fp8 48-block model vs exact fp64 model: {cos:.6f}", flush=True)
+    assert np.all(np.isfinite(v)) and cos >= 0.9976
+
+
+def _teacher_forced_blocks(full_dit, x, feats, t, gh, gw, St, txt_len, rows=None, sample=(0, 23, 47)):
+    """Chains lens_block_forward through the 48 blocks from the oracle's
+    embeddings (img_in, txt_norm + txt_in, timestep MLP, fp32 as the residual
+    stream holds them) and, for each sampled block, runs the oracle block on
+    the GPU's own input to it: outputs at the parity bar, deltas at
+    DELTA_REL, over valid rows (rows: optional (image, text) row subsets)."""
+    T, dv = _env()
+    top = synth.top_weights()
+    B = x.shape[0]
+    ip, tp = synth.image_positions(gh, gw), synth.text_positions(St)
+    temb = O.timestep_embedding(top, t).astype(np.float32)
+    h_img = O.linear(x, top["img_in_w"], top["img_in_b"]).astype(np.float32)
+    h_txt = O.text_embed(top, feats).astype(np.float32)
+    cfg = T.default_config(T.LENS_BF16)
+    d_hi, d_ht = dv.upload(h_img), dv.upload(h_txt)
+    d_temb, d_ip, d_tp = dv.upload(temb), dv.upload(ip), dv.upload(tp)
+    d_tl = dv.upload(np.asarray(txt_len, np.int32)) if txt_len is not None else None
+    ws = dv.Workspace()
+    got = {}
+    for i, blk in enumerate(full_dit.blocks):
+        if i in sample:
+            torch.cuda.synchronize()
+            got[i] = [d_hi.cpu().numpy(), d_ht.cpu().numpy()]
+        dv.block_forward(cfg, blk, d_hi, d_ht, d_temb, d_ip, d_tp, d_tl, ws)
+        if i in sample:
+            torch.cuda.synchronize()
+            got[i] += [d_hi.cpu().numpy(), d_ht.cpu().numpy()]
+    assert np.all(np.isfinite(d_hi.cpu().numpy()))
+    ri_sel = np.arange(gh * gw) if rows is None else np.asarray(rows[0])
+    rt_sel = np.arange(St) if rows is None else np.asarray(rows[1])
+    tl = np.full(B, St) if txt_len is None else np.asarray(txt_len)
+    for i in sample:
+        hi_in, ht_in, hi_out, ht_out = got[i]
+        print(f"oracle block {i} (teacher-forced)", flush=True)
+        ri, rt = O.block_forward(synth.block_weights(i), hi_in, ht_in, temb, ip, tp, txt_len, rows=rows)
+        gi, hi0 = hi_out[:, ri_sel], hi_in[:, ri_sel]
+        assert_parity(gi, ri, f"block {i} h_img", rel=MAXABS_REL)
+        assert_parity(gi - hi0, ri - hi0, f"block {i} delta_img", rel=DELTA_REL)
+        if St:
+            keep = [rt_sel < tl[b] for b in range(B)]
+            pick = lambda a: np.concatenate([a[b][keep[b]] for b in range(B)])
+            gt, ht0 = pick(ht_out[:, rt_sel]), pick(ht_in[:, rt_sel])
+            rv = pick(rt)
+            assert_parity(gt, rv, f"block {i} h_txt", rel=MAXABS_REL)
+            assert_parity(gt - ht0, rv - ht0, f"block {i} delta_txt", rel=DELTA_REL)
+
+
+@pytest.mark.timeout(900)
+def test_dit_teacher_forced_blocks_1024_cfg_batch(full_dit):
+    """Blocks 0, 23, 47 of the benchmarked launch: 1024^2, cond + uncond
+    (shared latent and t, independent text features), all rows."""
+    print("teacher-forced blocks 0/23/47, 1024^2, B = 2 (CFG)", flush=True)
+    x0 = synth.bf16_round(synth.latents(1, 4096))
+    x = np.concatenate([x0, x0])
+    feats = np.concatenate([synth.text_features(1, 512, seed=synth.SEED_TEXT_COND),
+                            synth.text_features(1, 512, seed=synth.SEED_TEXT_UNCOND)])
+    _teacher_forced_blocks(full_dit, x, feats, np.array([0.75, 0.75]), 64, 64, 512, None)
+
+
+@pytest.mark.timeout(900)
+def test_dit_teacher_forced_blocks_1440_turbo(full_dit):
+    """1440^2 (90 x 90 = 8100 image + 512 text tokens), B = 1, the first
+    Turbo step (t = 1, no CFG); every 4th image row and all text rows."""
+    print("teacher-forced blocks 0/23/47, 1440^2, B = 1", flush=True)
+    x = synth.bf16_round(synth.latents(1, 8100))
+    feats = synth.text_features(1, 512, seed=synth.SEED_TEXT_COND)
+    _teacher_forced_blocks(full_dit, x, feats, np.array([1.0]), 90, 90, 512, None,
+                           rows=(np.arange(0, 8100, 4), np.arange(512)))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("gh,gw", [(45, 90), (90, 45)])
+def test_dit_teacher_forced_blocks_aspect_batch8(full_dit, gh, gw):
+    """2:1 and 1:2 aspect (4050 image tokens), 4 latents with CFG (batch 8),
+    text lengths drawn from 64..512 and padded to 512 with the key mask, at
+    the middle of a 50-step loop (t = 0.5); every 8th image row and all
+    valid text rows."""
+    print(f"teacher-forced blocks 0/23/47, {gh}x{gw}, B = 8 (CFG), masked text", flush=True)
+    xs = synth.bf16_round(synth.latents(4, gh * gw))
+    x = np.concatenate([xs, xs])
+    tl = np.concatenate([synth.text_lengths(4, 64, 512, stream=0), synth.text_lengths(4, 64, 512, stream=1)])
+    fc = synth.text_features(4, 512, seed=synth.SEED_TEXT_COND, txt_len=tl[:4])
+    fu = synth.text_features(4, 512, seed=synth.SEED_TEXT_UNCOND, txt_len=tl[4:])
+    _teacher_forced_blocks(full_dit, x, np.concatenate([fc, fu]), np.full(8, 0.5), gh, gw, 512, tl,
+                           rows=(np.arange(0, gh * gw, 8), np.arange(512)))
+
+
 def test_dit_fp8_full_48_blocks_1024(full_dit):
     """The MX fp8 variant of the benchmarked launch (projection weights
     quantized on the device from the same bf16 model): the same properties,
     and per sample the pages' low-precision gate (cosine >= 0.9976 of the
     quantized DiT's output against the unquantized one, Lens-3.8B-4bit
-    article, section 4) with the bf16 model as the unquantized one, since
-    the fp64 oracle is out of reach at this size (measured 0.9992-0.9993;
-    at two blocks the fp8 denoiser meets the gate against the fp64 model)."""
+    article, section 4) against the bf16 model (measured 0.9992-0.9993; at
+    B = 1 the same fp8 model is held to the gate against the exact fp64
+    model above)."""
     T, dv = _env()
     print("dit 48 blocks fp8 1024^2 B=2", flush=True)
     v16 = _full_run_props(T.default_config(T.LENS_BF16), full_dit)

@@ -65,7 +65,7 @@ def test_mxfp8_quantize_bit_exact(dtype, layout):
     np.testing.assert_array_equal(s - 127, ev)
 
 
-def run_block_fp8(B, gh, gw, St, txt_len=None, variant="canonical"):
+def run_block_fp8(B, gh, gw, St, txt_len=None, variant="canonical", biases=True):
     dv = _dev()
     import text_image_flow_amd as T
     cfg = T.default_config(T.LENS_BF16)
@@ -73,6 +73,8 @@ def run_block_fp8(B, gh, gw, St, txt_len=None, variant="canonical"):
     Si = gh * gw
     print(f"fp8 block B={B} grid={gh}x{gw} S_txt={St} txt_len={txt_len} variant={variant}", flush=True)
     w = synth.block_weights(0, dtype="bf16", variant=variant)
+    if not biases:
+        w = synth.without_biases(w)
     h_img, h_txt, temb = synth.block_inputs(B, Si, St, dtype="bf16", seed=1)
     ip, tp = synth.image_positions(gh, gw), synth.text_positions(St)
     blk = dv.DeviceBlock(w, T.LENS_BF16, gemm_fp8=True)
@@ -101,24 +103,40 @@ def _check_fp8_delta(name, g, r8, rx, h):
     its distance to the exact block at most 1.15x the oracle fp8 block's
     (measured 1.00x); (2) it is the same fp8 computation -- the RMS of its
     difference to the oracle's fp8 block at most 0.04 x RMS(delta) (measured
-    0.017-0.023 at 256 to 4096 image tokens) and delta cosine >= 0.999."""
+    0.017-0.023 at 256 to 4096 image tokens) and delta cosine >= 0.999.
+    Element-wise: (3) the GPU's largest error against the exact block is at
+    most 1.25x the oracle fp8 block's largest error M (both are the same
+    quantization noise, whose maximum over this many elements varies by a
+    few per cent from one draw to another); (4) hence, by the triangle
+    inequality |g - r8| <= |g - rx| + |r8 - rx|, no element of the GPU
+    delta is further than 2.25 M from the oracle fp8 block's."""
     dg, d8, dx = (g - h).ravel(), (r8 - h).ravel(), (rx - h).ravel()
     e_gpu, e_ora = _rms(dg - dx), _rms(d8 - dx)
     rd = _rms(d8)
+    m_gpu, m_ora, m_diff = (float(np.max(np.abs(a))) for a in (dg - dx, d8 - dx, dg - d8))
     cos = float(dg @ d8 / np.linalg.norm(dg) / np.linalg.norm(d8))
     msg = (f"{name}: |gpu-exact| {e_gpu / rd:.4f}, |fp8 oracle-exact| {e_ora / rd:.4f}, "
-           f"|gpu-fp8 oracle| {_rms(dg - d8) / rd:.4f} (x RMS(delta)), cos {cos:.6f}")
+           f"|gpu-fp8 oracle| {_rms(dg - d8) / rd:.4f} (RMS, x RMS(delta)), cos {cos:.6f}; "
+           f"max |gpu-exact| {m_gpu / rd:.4f}, max |fp8 oracle-exact| {m_ora / rd:.4f}, "
+           f"max |gpu-fp8 oracle| {m_diff / rd:.4f} (x RMS(delta))")
     print(msg, flush=True)
     assert np.all(np.isfinite(g)), name
     assert e_gpu <= 1.15 * e_ora, msg
     assert _rms(dg - d8) <= 0.04 * rd and cos >= 0.999, msg
+    assert m_gpu <= 1.25 * m_ora, msg
+    assert m_diff <= 2.25 * m_ora, msg
 
 
-@pytest.mark.parametrize("case", [(1, 16, 16, 32, None), (2, 10, 13, 45, [45, 17])])
+@pytest.mark.parametrize("case", [(1, 16, 16, 32, None, True), (2, 10, 13, 45, [45, 17], True),
+                                  (2, 10, 13, 45, [45, 17], False)])
 def test_block_fp8_parity(case):
-    B, gh, gw, St, tl = case
-    gi, gt, ri, rt, hi, ht = run_block_fp8(B, gh, gw, St, tl)
+    """Ragged and masked shapes; the last case without any bias (NULL bias
+    pointers through the fp8 QKV, gated and MX SwiGLU epilogues)."""
+    B, gh, gw, St, tl, biases = case
+    gi, gt, ri, rt, hi, ht = run_block_fp8(B, gh, gw, St, tl, biases=biases)
     w = synth.block_weights(0, dtype="bf16")
+    if not biases:
+        w = synth.without_biases(w)
     h_img, h_txt, temb = synth.block_inputs(B, gh * gw, St, dtype="bf16", seed=1)
     xi, xt = O.block_forward(w, h_img, h_txt, temb, synth.image_positions(gh, gw), synth.text_positions(St), tl)
     _check_fp8_delta("img", gi, ri, xi, hi)
