@@ -110,3 +110,29 @@ def budget(variant, B, gh, gw, St, txt_len=None, block=0, seed_h=1, biases=True)
         res["out"] = max(res["out"], err / float(np.sqrt(np.mean(x * x))))
         res["delta"] = max(res["delta"], err / float(np.sqrt(np.mean((x - h) ** 2))))
     return res
+
+
+def budget_model_block(block=0, t=0.75):
+    """The same budget for a block of the whole model at its own modulation:
+    the 1024^2 cond + uncond launch (B = 2, one latent, cond and uncond text),
+    h from the oracle's img_in / txt_in and temb from its timestep MLP at t
+    (fp32, as the residual stream holds them), block `block` of the seeded
+    model.  Returns {'out': ratio, 'delta': ratio} as budget()."""
+    top = synth.top_weights()
+    x0 = synth.bf16_round(synth.latents(1, 4096))
+    x = np.concatenate([x0, x0])
+    feats = np.concatenate([synth.text_features(1, 512, seed=synth.SEED_TEXT_COND),
+                            synth.text_features(1, 512, seed=synth.SEED_TEXT_UNCOND)])
+    temb = O.timestep_embedding(top, np.array([t, t])).astype(np.float32)
+    hi = O.linear(x, top["img_in_w"], top["img_in_b"]).astype(np.float32)
+    ht = O.text_embed(top, feats).astype(np.float32)
+    ip, tp = synth.image_positions(64, 64), synth.text_positions(512)
+    w = synth.block_weights(block)
+    xi, xt = O.block_forward(w, hi, ht, temb, ip, tp)
+    ri, rt = block_forward_rounded(w, hi, ht, temb, ip, tp)
+    res = {"out": 0.0, "delta": 0.0}
+    for x_, r_, h_ in ((xi, ri, hi), (xt, rt, ht)):
+        err = float(np.max(np.abs(r_ - x_)))
+        res["out"] = max(res["out"], err / float(np.sqrt(np.mean(x_ * x_))))
+        res["delta"] = max(res["delta"], err / float(np.sqrt(np.mean((x_ - h_) ** 2))))
+    return res

@@ -8,8 +8,8 @@ and the canonical bars must stay within 2.5x of it, so they cannot drift
 loose unnoticed.  CPU only."""
 import pytest
 
-from tests.parity import DELTA_REL, LATE_DELTA_REL, LATE_OUT_REL, MAXABS_REL, SHARP_DELTA_REL
-from tests.rounding_model import budget
+from tests.parity import DELTA_REL, LATE_DELTA_REL, LATE_OUT_REL, MAXABS_REL, MODEL_DELTA_REL, SHARP_DELTA_REL
+from tests.rounding_model import budget, budget_model_block
 
 # (name, variant, B, grid h, grid w, S_txt, txt_len, biases, out bar, delta bar, tight)
 CASES = [
@@ -36,6 +36,18 @@ def _check(name, variant, B, gh, gw, St, tl, biases, out_bar, delta_bar, tight):
     assert out_bar >= 1.25 * b["out"] and delta_bar >= 1.25 * b["delta"], msg
     if tight:
         assert delta_bar <= 2.5 * b["delta"], msg
+
+
+@pytest.mark.slow
+def test_model_block_bar_covers_rounding_budget():
+    """Block 0 of the 48-block model at the 1024^2 cond + uncond launch, from
+    the oracle's embeddings (the teacher-forced GPU checks)."""
+    b = budget_model_block(0, 0.75)
+    msg = (f"model block 0: budget out {b['out']:.4f} delta {b['delta']:.4f}; bars out {MAXABS_REL} "
+           f"delta {MODEL_DELTA_REL}")
+    print(msg)
+    assert MAXABS_REL >= 1.25 * b["out"] and MODEL_DELTA_REL >= 1.25 * b["delta"], msg
+    assert MODEL_DELTA_REL <= 2.5 * b["delta"], msg
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
