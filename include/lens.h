@@ -192,6 +192,28 @@ lens_status lens_dit_forward(const lens_config *cfg, const lens_dit_w *w, const 
                              void *workspace, size_t ws_bytes, void *hip_stream);
 
 /*
+ * lens_dit_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, computation and results
+ * as lens_dit_forward; its scratch is a file-scope device array of
+ * LENS_NOALLOC_SCRATCH_BYTES (384 MiB: the 1024^2 cond + uncond launch, B = 2,
+ * needs 274 MiB in bf16 and 325 MiB with gemm_fp8; 1440^2 at B = 1 needs
+ * 245 MiB) that every GPU the library runs on holds from the library's load
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  A call whose lens_dit_workspace_bytes exceeds
+ * LENS_NOALLOC_SCRATCH_BYTES returns LENS_ERR_WORKSPACE before any device
+ * work.  All calls on one GPU share that GPU's array and nothing of one call
+ * carries into the next (each call writes every intermediate before reading
+ * it); calls that overlap on one GPU (other streams, other threads) race on
+ * it and must be serialised by the caller.
+ */
+#define LENS_NOALLOC_SCRATCH_BYTES ((size_t)384 << 20)
+lens_status lens_dit_forward_noalloc(const lens_config *cfg, const lens_dit_w *w, const void *x,
+                                     const void *txt_feats, const float *t, const int32_t *img_pos,
+                                     const int32_t *txt_pos, const int32_t *txt_len, int32_t B, int32_t S_img,
+                                     int32_t S_txt, float *v_out, void *hip_stream);
+
+/*
  * Flow-matching Euler step with optional classifier-free guidance, on n
  * elements:  v = v_uncond + cfg_scale (v_cond - v_uncond)  (v = v_cond when
  * v_uncond is NULL);  x <- x + dt v.

@@ -188,3 +188,29 @@ def test_fp8_argument_checks():
     assert T.lens_block_workspace_bytes(cfg, 1, 16, 8) == 0
     cfg.gemm_fp8 = 1
     assert T.lens_block_workspace_bytes(cfg, 1, 16, 8) > T.lens_block_workspace_bytes(T.default_config(L.LENS_BF16), 1, 16, 8)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """lens_dit_forward_noalloc checks the call's scratch need against the
+    static array before any device work: 2:1 at batch 8 (1.08 GiB) is
+    refused with LENS_ERR_WORKSPACE; invalid arguments as lens_dit_forward."""
+    c = T.default_config(T.LENS_BF16)
+    c.n_blocks = 1
+    blk = (T.LensBlockW * 1)()
+    for s in ("img", "txt"):
+        sw = getattr(blk[0], s)
+        for n in ("mod", "qkv", "out", "w1", "w3", "w2"):
+            getattr(sw, n).w = 0x1000
+        sw.q_gain = sw.k_gain = 0x1000
+    d = T.LensDitW()
+    for n in ("t_fc1", "t_fc2", "img_in", "txt_in", "norm_out", "proj_out"):
+        getattr(d, n).w = 0x1000
+    d.txt_gain = 0x1000
+    d.blocks = C.cast(blk, C.POINTER(T.LensBlockW))
+    assert T.lens_dit_workspace_bytes(c, 8, 4050, 512) > L.NOALLOC_SCRATCH_BYTES
+    st = L.lens_dit_forward_noalloc(c, d, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 8, 4050, 512, 0x1000, None)
+    assert st == L.LENS_ERR_WORKSPACE and "static scratch" in T.last_error(), T.last_error()
+    st = L.lens_dit_forward_noalloc(c, d, None, 0x1000, 0x1000, 0x1000, 0x1000, None, 1, 16, 8, 0x1000, None)
+    assert st == L.LENS_ERR_INVALID_ARG
+    st = L.lens_dit_forward_noalloc(c, d, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 0, 16, 8, 0x1000, None)
+    assert st == L.LENS_ERR_INVALID_ARG

@@ -22,7 +22,7 @@ KERNEL_NAMES = ("gemm", "attention", "norm", "qknorm_rope", "adaln")
 # every function lens.h declares (checked against the header by the tests)
 EXPORTS = (
     "lens_default_config", "lens_block_workspace_bytes", "lens_dit_workspace_bytes", "lens_block_forward",
-    "lens_dit_forward", "lens_flow_step", "lens_flow_step_rescaled", "lens_quantize_mxfp8", "lens_timer_start",
+    "lens_dit_forward", "lens_dit_forward_noalloc", "lens_flow_step", "lens_flow_step_rescaled", "lens_quantize_mxfp8", "lens_timer_start",
     "lens_timer_stop", "lens_time_grid", "lens_mu_for_tokens",
     "lens_status_string",
     "lens_last_error", "lens_version",
@@ -81,6 +81,7 @@ def lib() -> C.CDLL:
             "lens_dit_workspace_bytes": (SZ, [cfgp, I32, I32, I32]),
             "lens_block_forward": (C.c_int, [cfgp, C.POINTER(LensBlockW), P, P, P, P, P, P, I32, I32, I32, P, SZ, P]),
             "lens_dit_forward": (C.c_int, [cfgp, C.POINTER(LensDitW), P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]),
+            "lens_dit_forward_noalloc": (C.c_int, [cfgp, C.POINTER(LensDitW), P, P, P, P, P, P, I32, I32, I32, P, P]),
             "lens_flow_step": (C.c_int, [P, P, P, I64, F, F, P, C.c_int, P]),
             "lens_flow_step_rescaled": (C.c_int, [P, P, P, I64, I32, F, F, P, C.c_int, P]),
             "lens_quantize_mxfp8": (C.c_int, [P, C.c_int, I64, I32, I32, P, P, P]),
@@ -141,6 +142,15 @@ def lens_dit_forward(cfg, w, x, txt_feats, t, img_pos, txt_pos, txt_len, B, S_im
                      ws_bytes, stream) -> int:
     return lib().lens_dit_forward(C.byref(cfg), C.byref(w), x, txt_feats, t, img_pos, txt_pos, txt_len, B, S_img,
                                   S_txt, v_out, workspace, ws_bytes, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 384 << 20   # LENS_NOALLOC_SCRATCH_BYTES of lens.h
+
+
+def lens_dit_forward_noalloc(cfg, w, x, txt_feats, t, img_pos, txt_pos, txt_len, B, S_img, S_txt, v_out,
+                             stream) -> int:
+    return lib().lens_dit_forward_noalloc(C.byref(cfg), C.byref(w), x, txt_feats, t, img_pos, txt_pos, txt_len, B,
+                                          S_img, S_txt, v_out, stream)
 
 
 def lens_flow_step(x, v_cond, v_uncond, n, dt, cfg_scale, x_lowp_out, lowp_dtype, stream) -> int:

@@ -7,6 +7,7 @@
 
 #include <cmath>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -482,10 +483,14 @@ lens_status lens_block_forward(const lens_config *c, const lens_block_w *w, floa
   return block_core(c, w, h_img, h_txt, mod_img, mod_txt, img_pos, txt_pos, txt_len, B, Si, St, ws, st);
 }
 
-lens_status lens_dit_forward(const lens_config *c, const lens_dit_w *w, const void *x, const void *txt_feats,
-                             const float *t, const int32_t *img_pos, const int32_t *txt_pos, const int32_t *txt_len,
-                             int32_t B, int32_t Si, int32_t St, float *v_out, void *workspace, size_t ws_bytes,
-                             void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of the whole-denoiser call, checked before any device work.
+lens_status check_dit_call(const lens_config *c, const lens_dit_w *w, const void *x, const void *txt_feats,
+                           const float *t, const int32_t *img_pos, const int32_t *txt_pos, int32_t B, int32_t Si,
+                           int32_t St, const float *v_out) {
   LTRY(check_dit_config(c));
   LTRY(check_sizes(B, Si, St));
   if (!w) return fail(LENS_ERR_INVALID_ARG, "weight table is NULL");
@@ -501,17 +506,18 @@ lens_status lens_dit_forward(const lens_config *c, const lens_dit_w *w, const vo
   if (!x || !t || !img_pos || !v_out) return fail(LENS_ERR_INVALID_ARG, "x, t, img_pos and v_out must not be NULL");
   if (St > 0 && (!txt_feats || !txt_pos))
     return fail(LENS_ERR_INVALID_ARG, "txt_feats and txt_pos must not be NULL");
-  const DitWs need = carve_dit(c, B, Si, St, nullptr);
-  if (!workspace || ws_bytes < need.bytes)
-    return fail(LENS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? ws_bytes : 0, need.bytes);
-  if ((uintptr_t)workspace % 256) return fail(LENS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return LENS_OK;
+}
 
-  hipStream_t st = (hipStream_t)hip_stream;
+// The whole denoiser on a checked call, with its scratch at `base` (256-byte
+// aligned, carve_dit(...).bytes long).
+lens_status dit_run(const lens_config *c, const lens_dit_w *w, const void *x, const void *txt_feats, const float *t,
+                    const int32_t *img_pos, const int32_t *txt_pos, const int32_t *txt_len, int32_t B, int32_t Si,
+                    int32_t St, float *v_out, char *base, hipStream_t st) {
   const bool bf = c->act_dtype == LENS_BF16;
-  const DitWs ws = carve_dit(c, B, Si, St, (char *)workspace);
+  const DitWs ws = carve_dit(c, B, Si, St, base);
   const int D = c->hidden;
   hipError_t e;
-
   // timestep embedding: phi(t) -> fc1 -> SiLU -> fc2
   HIP_TRY(launch_timestep_features(t, ws.phi, B, c->t_freq_dim, c->t_scale, st));
   {
@@ -575,6 +581,67 @@ lens_status lens_dit_forward(const lens_config *c, const lens_dit_w *w, const vo
                   c->out_ch, D};
   LTRY(gemm(LENS_KERNEL_GEMM, EPI_STORE_F32, bf, &g, 1, st));
   return LENS_OK;
+}
+
+// File-scope device scratch of lens_dit_forward_noalloc.  Every device the
+// library runs on holds its own copy from the load of this code object until
+// the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in there).
+static __device__ __align__(256) unsigned char scratch[LENS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's scratch, looked up once per device.
+lens_status static_scratch(void **out) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LENS_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LENS_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LENS_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return LENS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lens_status lens_dit_forward(const lens_config *c, const lens_dit_w *w, const void *x, const void *txt_feats,
+                             const float *t, const int32_t *img_pos, const int32_t *txt_pos, const int32_t *txt_len,
+                             int32_t B, int32_t Si, int32_t St, float *v_out, void *workspace, size_t ws_bytes,
+                             void *hip_stream) {
+  LTRY(check_dit_call(c, w, x, txt_feats, t, img_pos, txt_pos, B, Si, St, v_out));
+  const DitWs need = carve_dit(c, B, Si, St, nullptr);
+  if (!workspace || ws_bytes < need.bytes)
+    return fail(LENS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? ws_bytes : 0, need.bytes);
+  if ((uintptr_t)workspace % 256) return fail(LENS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return dit_run(c, w, x, txt_feats, t, img_pos, txt_pos, txt_len, B, Si, St, v_out, (char *)workspace,
+                 (hipStream_t)hip_stream);
+}
+
+lens_status lens_dit_forward_noalloc(const lens_config *c, const lens_dit_w *w, const void *x, const void *txt_feats,
+                                     const float *t, const int32_t *img_pos, const int32_t *txt_pos,
+                                     const int32_t *txt_len, int32_t B, int32_t Si, int32_t St, float *v_out,
+                                     void *hip_stream) {
+  LTRY(check_dit_call(c, w, x, txt_feats, t, img_pos, txt_pos, B, Si, St, v_out));
+  const DitWs need = carve_dit(c, B, Si, St, nullptr);
+  if (need.bytes > LENS_NOALLOC_SCRATCH_BYTES)
+    return fail(LENS_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                need.bytes, (size_t)LENS_NOALLOC_SCRATCH_BYTES);
+  void *base = nullptr;
+  LTRY(static_scratch(&base));
+  return dit_run(c, w, x, txt_feats, t, img_pos, txt_pos, txt_len, B, Si, St, v_out, (char *)base,
+                 (hipStream_t)hip_stream);
 }
 
 lens_status lens_flow_step(float *x, const float *v_cond, const float *v_uncond, int64_t n, float dt,
