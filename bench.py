@@ -19,8 +19,11 @@ roofline of the dominant kernel family.  `cpu_baseline` times the fp64
 oracle on a bounded sample (one block at the same shape) on the host cores.
 `fp8_variant` times the same step with the block projections as MX fp8
 GEMMs (weights quantized on the device from the same bf16 weights) and
-reports the cosine of its velocity against the bf16 step's on one input;
-`value` is always the bf16 step.
+reports the cosine of its velocity against the bf16 step's on one input.
+`turbo_1440` times a second workload: whole 4-step Turbo-style sampling
+jobs at 1440x1440 (90 x 90 = 8100 image tokens + 512 text tokens, batch 1,
+no CFG), with its own kernel breakdown and roofline.  `value` is always the
+bf16 1024x1024 CFG step.
 """
 from __future__ import annotations
 
@@ -41,6 +44,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 S_IMG, S_TXT, GRID = 4096, 512, (64, 64)
 CFG_SCALE = 5.0
 LOOP_STEPS = 20
+# Turbo-style sampling at 1440^2: 90 x 90 image tokens + 512 text tokens,
+# batch 1, 4 Euler steps, no CFG (guidance 1.0)
+TURBO_GRID, TURBO_TXT, TURBO_STEPS = (90, 90), 512, 4
 
 
 def block_flops(d, S_img, S_txt, B, q_valid=None, kv_valid=None):
@@ -106,6 +112,93 @@ def measured_traffic():
     return float(fields["traffic_bytes_per_launch"])
 
 
+def family_roofline(L, ms, n, steps, fam_flops):
+    """Per-family breakdown from the library's kernel timer and the
+    roofline of the dominant MFMA family (gemm or attention)."""
+    kernels = {}
+    for i, name in enumerate(L.KERNEL_NAMES):
+        if n[i] == 0:
+            continue
+        e = {"ms_per_step": round(ms[i] / steps, 4), "launches_per_step": n[i] // steps,
+             "avg_launch_us": round(1e3 * ms[i] / n[i], 2)}
+        if name in fam_flops:
+            e["TFLOP/s"] = round(fam_flops[name] / (ms[i] / steps * 1e-3) / 1e12, 1)
+        kernels[name] = e
+    dom = max(("gemm", "attention"), key=lambda k: kernels.get(k, {}).get("ms_per_step", 0))
+    i = L.KERNEL_NAMES.index(dom)
+    per_launch_flops = fam_flops[dom] / (n[i] / steps)
+    avg_s = ms[i] / n[i] * 1e-3
+    ach = per_launch_flops / avg_s / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flops_per_launch": per_launch_flops, "avg_launch_us": round(avg_s * 1e6, 2)}
+    return kernels, roof
+
+
+def turbo_sampling(d, cfg, dit, jobs, warmup, timer):
+    """One 1440^2 Turbo-style sampling job per repetition: 4 x
+    (lens_dit_forward at B = 1 + lens_flow_step without CFG) from the same
+    seeded latent, uniform time grid; inputs resident before timing."""
+    import torch
+    import synth
+    import text_image_flow_amd as T
+    from text_image_flow_amd import _lib as L
+    from text_image_flow_amd import device as dv
+    gh, gw = TURBO_GRID
+    S = gh * gw
+    x0 = synth.latents(1, S, d)
+    x_init = dv.upload(x0)
+    x = x_init.clone()
+    x_act = dv.upload(synth.bf16_round(x0), T.LENS_BF16)
+    x_act_init = x_act.clone()
+    feats = dv.upload(synth.text_features(1, TURBO_TXT, d, seed=synth.SEED_TEXT_COND), T.LENS_BF16)
+    ip, tp = dv.upload(synth.image_positions(gh, gw)), dv.upload(synth.text_positions(TURBO_TXT))
+    ts, dts = dv.time_grid(TURBO_STEPS)
+    t_tab = dv.upload(ts[:, None].copy())
+    v = torch.empty((1, S, d.out_ch), dtype=torch.float32, device="cuda")
+    ws = dv.Workspace()
+    ws.get(T.lens_dit_workspace_bytes(cfg, 1, S, TURBO_TXT))
+    torch.cuda.synchronize()
+
+    def job():
+        x.copy_(x_init)
+        x_act.copy_(x_act_init)
+        for k in range(TURBO_STEPS):
+            dv.dit_forward(cfg, dit, x_act, feats, t_tab[k], ip, tp, None, v, ws)
+            dv.flow_step(x, v, None, float(dts[k]), 1.0, x_act, T.LENS_BF16)
+
+    for _ in range(warmup):
+        job()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(jobs):
+        job()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_job = e0.elapsed_time(e1) / jobs
+    assert torch.isfinite(x).all().item(), "non-finite Turbo output"
+    fl = step_flops(d, S, TURBO_TXT, 1)
+    out = {"workload": "Lens MM-DiT Turbo-style sampling, 1440x1440", "image_tokens": S, "text_tokens": TURBO_TXT,
+           "batch": 1, "steps": TURBO_STEPS, "cfg": "none (guidance 1.0)", "jobs_timed": jobs,
+           "ms_per_job": round(ms_job, 3), "ms_per_step": round(ms_job / TURBO_STEPS, 3),
+           "TFLOP/s": round(fl["total"] * TURBO_STEPS / (ms_job * 1e-3) / 1e12, 2),
+           "pct_of_bf16_peak": round(100 * fl["total"] * TURBO_STEPS / (ms_job * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "flops_per_step": fl["total"], "kernels": None, "roofline": None}
+    if timer:
+        L.check(T.lens_timer_start((1 << L.LENS_KERNEL_COUNT) - 1))
+        torch.cuda.synchronize()
+        job()
+        torch.cuda.synchronize()
+        st, ms, n = T.lens_timer_stop()
+        L.check(st)
+        fam = {"gemm": fl["gemm_blocks"] + fl["gemm_embed"], "attention": fl["attention"],
+               "adaln": fl["adaln"] + fl["small"]}
+        out["kernels"], out["roofline"] = family_roofline(L, ms, n, TURBO_STEPS, fam)
+    return out
+
+
 def cpu_baseline(d):
     """The oracle as it stands, on one block at 1024^2 (B = 1), fp64."""
     import oracle as O
@@ -138,6 +231,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the MX fp8 variant")
     ap.add_argument("--no-b1", action="store_true",
                     help="skip the B = 1 forward and the clock-sampling pass (profiles of the B = 2 step alone)")
+    ap.add_argument("--no-turbo", action="store_true", help="skip the 1440^2 Turbo-style sampling workload")
     ap.add_argument("--copy-kernel-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (counter calibration) and exit")
     args = ap.parse_args()
@@ -273,23 +367,8 @@ def main():
         L.check(st)
         fam_flops = {"gemm": fl["gemm_blocks"] + fl["gemm_embed"], "attention": fl["attention"],
                      "adaln": fl["adaln"] + fl["small"]}
-        for i, name in enumerate(L.KERNEL_NAMES):
-            if n[i] == 0:
-                continue
-            e = {"ms_per_step": round(ms[i] / args.steps, 4), "launches_per_step": n[i] // args.steps,
-                 "avg_launch_us": round(1e3 * ms[i] / n[i], 2)}
-            if name in fam_flops:
-                e["TFLOP/s"] = round(fam_flops[name] / (ms[i] / args.steps * 1e-3) / 1e12, 1)
-            kernels[name] = e
-        dom = max(("gemm", "attention"), key=lambda k: kernels.get(k, {}).get("ms_per_step", 0))
-        i = L.KERNEL_NAMES.index(dom)
-        per_launch_flops = fam_flops[dom] / (n[i] / args.steps)
-        avg_s = ms[i] / n[i] * 1e-3
-        ach = per_launch_flops / avg_s / 1e12
-        traffic = measured_traffic() if dom == "gemm" else None
-        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "algorithmic_flops_per_launch": per_launch_flops, "avg_launch_us": round(avg_s * 1e6, 2)}
+        kernels, roof = family_roofline(L, ms, n, args.steps, fam_flops)
+        roof["traffic"] = measured_traffic() if roof["kernel"] == "gemm" else None
 
     # ---- MX fp8 variant of the same step (not the headline value)
     fp8 = None
@@ -332,6 +411,11 @@ def main():
                "format": "MX fp8: e4m3 elements, E8M0 scale per 32 along K, weights and activations of the "
                          "block projections (qkv, out, w1, w3, w2)", "kernels": fk}
 
+    # ---- 1440^2 Turbo-style sampling (a second workload, not the headline value)
+    turbo = None
+    if not args.no_turbo:
+        turbo = turbo_sampling(d, cfg, dit, max(1, min(args.steps, 3)), 1, not args.no_kernel_timer)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(d)
 
     out = {
@@ -346,7 +430,7 @@ def main():
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": fl["total"], "wall_s": round(wall, 3), "setup_s": round(setup_s, 1),
         "b1_forward": b1, "clock": clock,
-        "kernels": kernels, "roofline": roof, "cpu_baseline": cpu, "fp8_variant": fp8,
+        "kernels": kernels, "roofline": roof, "cpu_baseline": cpu, "fp8_variant": fp8, "turbo_1440": turbo,
     }
     print(json.dumps(out))
 

@@ -395,32 +395,47 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
   return LENS_OK;
 }
 
+// AdaLN modulation of `nblk` blocks from SiLU(temb), plus, when extra is not
+// NULL, one more GEMV of the same input (the final layer's modulation, N =
+// extra_n, into extra_y).  mods: [nblk][2][B][6D].  The problems go out in
+// as few launches of at most GEMV_MAX_PROBS as there can be, split evenly.
 lens_status adaln_all(const lens_config *c, const lens_block_w *const *blocks, int nblk, const float *temb, int B,
-                      float *mods, hipStream_t st) {
-  // mods: [nblk][2][B][6D]; problems in chunks of GEMV_MAX_PROBS
+                      float *mods, hipStream_t st, const lens_linear *extra = nullptr, float *extra_y = nullptr,
+                      int extra_n = 0) {
   const bool bf = c->act_dtype == LENS_BF16;
   const int D = c->hidden, D6 = 6 * D;
+  const int total = 2 * nblk + (extra ? 1 : 0);
+  const int launches = (total + GEMV_MAX_PROBS - 1) / GEMV_MAX_PROBS;
   GemvBatch gb{};
+  int done = 0, launched = 0;
   auto flush = [&]() -> lens_status {
     if (gb.nprob == 0) return LENS_OK;
     Timed t(LENS_KERNEL_ADALN, st);
     hipError_t e = t.done(launch_gemv(gb, temb, B, D, true, bf, st));
+    done += gb.nprob;
+    ++launched;
     gb.nprob = 0;
     if (e != hipSuccess) return fail(LENS_ERR_HIP, "AdaLN launch failed: %s", hipGetErrorString(e));
     return LENS_OK;
   };
+  // problems of the current launch: an even share of what is left
+  auto share = [&]() { return (total - done + (launches - launched) - 1) / (launches - launched); };
+  auto add = [&](const void *w, const void *b, float *y, int n) -> lens_status {
+    const int k = gb.nprob++;
+    gb.W[k] = w;
+    gb.bias[k] = b;
+    gb.y[k] = y;
+    gb.N[k] = n;
+    gb.y_stride[k] = n;
+    return gb.nprob == share() ? flush() : LENS_OK;
+  };
   for (int i = 0; i < nblk; ++i) {
     for (int s = 0; s < 2; ++s) {
       const lens_linear &l = s == 0 ? blocks[i]->img.mod : blocks[i]->txt.mod;
-      const int k = gb.nprob++;
-      gb.W[k] = l.w;
-      gb.bias[k] = l.b;
-      gb.y[k] = mods + ((size_t)i * 2 + s) * B * D6;
-      gb.N[k] = D6;
-      gb.y_stride[k] = D6;
-      if (gb.nprob == GEMV_MAX_PROBS) LTRY(flush());
+      LTRY(add(l.w, l.b, mods + ((size_t)i * 2 + s) * B * D6, D6));
     }
   }
+  if (extra) LTRY(add(extra->w, extra->b, extra_y, extra_n));
   return flush();
 }
 
@@ -542,17 +557,7 @@ lens_status dit_run(const lens_config *c, const lens_dit_w *w, const void *x, co
   {
     std::vector<const lens_block_w *> bl(c->n_blocks);
     for (int i = 0; i < c->n_blocks; ++i) bl[i] = &w->blocks[i];
-    LTRY(adaln_all(c, bl.data(), c->n_blocks, ws.temb, B, ws.mods, st));
-    GemvBatch gb{};
-    gb.nprob = 1;
-    gb.W[0] = w->norm_out.w;
-    gb.bias[0] = w->norm_out.b;
-    gb.y[0] = ws.nmod;
-    gb.N[0] = 2 * D;
-    gb.y_stride[0] = 2 * D;
-    Timed tt(LENS_KERNEL_ADALN, st);
-    e = tt.done(launch_gemv(gb, ws.temb, B, D, true, bf, st));
-    if (e != hipSuccess) return fail(LENS_ERR_HIP, "norm_out modulation failed: %s", hipGetErrorString(e));
+    LTRY(adaln_all(c, bl.data(), c->n_blocks, ws.temb, B, ws.mods, st, &w->norm_out, ws.nmod, 2 * D));
   }
   // embeddings
   GemmProblem g{x, w->img_in.w, nullptr, w->img_in.b, nullptr, ws.h_img, nullptr, 0, 1, B * Si, D, c->in_ch};

@@ -196,8 +196,11 @@ hipError_t launch_qknorm_rope(const QkRopeArgs &a, bool bf16_path, hipStream_t s
 
 // Skinny GEMM (GEMV over a small batch): y[b, n] = sum_k f(x[b, k]) W[n, k] + bias[n],
 // f = SiLU when silu_in, else identity.  x float [B, K], y float [B, N] rows at
-// y + b * y_stride.  Up to GEMV_MAX_PROBS problems share x, B and K.
-constexpr int GEMV_MAX_PROBS = 24;
+// y + b * y_stride.  Up to GEMV_MAX_PROBS problems share x, B and K (25: the
+// 96 AdaLN matrices of 48 blocks and the final layer's modulation go out in
+// four launches; the batch, passed by value, stays under 1 KB of kernel
+// arguments).
+constexpr int GEMV_MAX_PROBS = 25;
 struct GemvBatch {
   const void *W[GEMV_MAX_PROBS];
   const void *bias[GEMV_MAX_PROBS];

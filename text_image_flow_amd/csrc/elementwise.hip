@@ -39,9 +39,24 @@ __device__ __forceinline__ void store4<bf16>(bf16 *dst, float a, float b, float 
 
 // ------------------------------------------------ RMSNorm + modulation
 // norm_rw(MX) rows per wave; D % 256 == 0 so each lane owns D/256 float4
-// groups of a row.  Two rows per wave for bf16 output, four for MX fp8
-// output (measured: 4 rows cost the bf16 kernel 3 % and save the MX one 7 %).
-constexpr int norm_rw(bool mx) { return mx ? 4 : 2; }
+// groups of a row.  Three rows per wave for bf16 / fp32 output, four for MX
+// fp8 output.  The normalized rows are stored non-temporally (they are read
+// once, by the next GEMM, long after this kernel's other traffic).  Measured
+// on MI355X at 1024^2 (9216 rows of 1536, h just written by the previous
+// GEMM): 3 rows + non-temporal stores 14.1 us, 2 rows + ordinary stores
+// 15.5 us; non-temporal loads of h are slower there (h is still in cache).
+constexpr int norm_rw(bool mx) { return mx ? 4 : 3; }
+
+template <typename T>
+__device__ __forceinline__ void store4_nt(T *dst, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4_nt<float>(float *dst, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(f32x4{a, b, c, d}, (f32x4 *)dst);
+}
+template <>
+__device__ __forceinline__ void store4_nt<bf16>(bf16 *dst, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d}, (bf16x4 *)dst);
+}
 
 template <typename T, int G, bool MX = false>
 __global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, NormModProblem p1, int split0,
@@ -109,8 +124,8 @@ __global__ __launch_bounds__(256) void norm_modulate_kernel(NormModProblem p0, N
 #pragma unroll
       for (int i = 0; i < G; ++i) {
         const int c = (i * 64 + lane) * 4;
-        store4<T>(out + c, v[i].x * rs * (1.f + s4[i].x) + h4[i].x, v[i].y * rs * (1.f + s4[i].y) + h4[i].y,
-                  v[i].z * rs * (1.f + s4[i].z) + h4[i].z, v[i].w * rs * (1.f + s4[i].w) + h4[i].w);
+        store4_nt<T>(out + c, v[i].x * rs * (1.f + s4[i].x) + h4[i].x, v[i].y * rs * (1.f + s4[i].y) + h4[i].y,
+                     v[i].z * rs * (1.f + s4[i].z) + h4[i].z, v[i].w * rs * (1.f + s4[i].w) + h4[i].w);
       }
     }
     if (more) {
@@ -321,15 +336,20 @@ hipError_t gemv_run(const GemvBatch &g, const float *x, int K, bool silu_in, hip
 }
 
 // bf16 weights: a persistent grid (GEMV_BLOCKS_PER_CU blocks per CU) walks
-// the rows of all problems of the batch as one index space, each wave a
-// contiguous run of rows, so no tail of half-empty rounds is left.  The
-// block stages f(x) for all its samples in LDS once (f is SiLU when
-// silu_in).  A wave takes GEMV_RG rows at a time with their 16-byte weight
-// loads for all KC k-chunks (lane l owns k = 512 c + 8 l .. + 7) in flight
-// together; f(x) comes from LDS as it is used, so few VGPRs are live and
-// several waves fit per SIMD.  The RG x NB lane partials are reduced by a
-// transposing butterfly: every exchange step halves the values a lane
-// holds, so the sums cost about RG x NB shuffles instead of 6 each.
+// the rows of all problems of the batch as one index space in groups of
+// GEMV_RG rows, group g going to wave g mod (waves of the grid), so at any
+// time the grid streams one contiguous stretch of the weights.  The block
+// stages f(x) for all its samples in LDS once (f is SiLU when silu_in).  A
+// wave takes one group at a time with its 16-byte weight loads for all KC
+// k-chunks (lane l owns k = 512 c + 8 l .. + 7) in flight together, loaded
+// non-temporally (each weight is read once per call); f(x) comes from LDS
+// as it is used, so few VGPRs are live and several waves fit per SIMD.
+// Measured on MI355X for the 24 AdaLN matrices of 12 blocks (680 MB of
+// weights, B = 2): 108 us per launch (6.3 TB/s) against 138 us with
+// ordinary loads and a contiguous run of rows per wave.  The RG x NB lane
+// partials are reduced by a transposing butterfly: every exchange step
+// halves the values a lane holds, so the sums cost about RG x NB shuffles
+// instead of 6 each.
 constexpr int GEMV_RG = 4;               // rows per group (loads in flight together)
 constexpr int GEMV_BLOCKS_PER_CU = 4;
 
@@ -338,9 +358,13 @@ struct pow2_ceil { static constexpr int v = N <= 1 ? 1 : 2 * pow2_ceil<(N + 1) /
 template <>
 struct pow2_ceil<1> { static constexpr int v = 1; };
 
+__device__ __forceinline__ bf16x8 load_weights_nt(const bf16 *p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4 *)p));
+}
+
 template <int NB, int KC>
 __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvBatch g, const float *x, int K, int silu_in,
-                                                        int total_rows, int rows_per_wave) {
+                                                        int total_rows) {
   __shared__ __attribute__((aligned(16))) float sx[NB * GEMV_MAXK];
   for (int i = threadIdx.x; i < NB * K; i += 256) {
     const float v = x[i];
@@ -349,17 +373,17 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvBatch g, const float
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r_begin = (blockIdx.x * GEMV_WAVES + wave) * rows_per_wave;
-  const int r_end = min(total_rows, r_begin + rows_per_wave);
+  const int r_begin = (blockIdx.x * GEMV_WAVES + wave) * GEMV_RG;
+  const int r_step = gridDim.x * GEMV_WAVES * GEMV_RG;
+  const int r_end = total_rows;
   if (r_begin >= r_end) return;
-  // problem of the wave's first row
+  // problem of the wave's current row (rows only increase along the walk)
   int prob = 0, pbase = 0;
-  while (prob + 1 < g.nprob && r_begin >= pbase + g.N[prob]) pbase += g.N[prob++];
   constexpr int NV = GEMV_RG * NB, VP = pow2_ceil<NV>::v;
   static_assert(VP <= 64, "values per lane");
 #pragma unroll 1
-  for (int r0 = r_begin; r0 < r_end; r0 += GEMV_RG) {
-    // each row's problem and row inside it (rows past the run repeat the last)
+  for (int r0 = r_begin; r0 < r_end; r0 += r_step) {
+    // each row's problem and row inside it (rows past the end repeat the last)
     int rp[GEMV_RG], rn[GEMV_RG];
 #pragma unroll
     for (int r = 0; r < GEMV_RG; ++r) {
@@ -374,7 +398,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvBatch g, const float
       const int k = c * 512 + lane * 8;
 #pragma unroll
       for (int r = 0; r < GEMV_RG; ++r)
-        wv[c][r] = k < K ? *(const bf16x8 *)((const bf16 *)g.W[rp[r]] + (int64_t)rn[r] * K + k) : bf16x8{};
+        wv[c][r] = k < K ? load_weights_nt((const bf16 *)g.W[rp[r]] + (int64_t)rn[r] * K + k) : bf16x8{};
     }
     float v[VP];
 #pragma unroll
@@ -437,11 +461,11 @@ hipError_t gemv_bf16_run(const GemvBatch &g, const float *x, int K, bool silu_in
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
     cus = c;
   }
-  const int waves = cus * GEMV_BLOCKS_PER_CU * GEMV_WAVES;
-  int rpw = (total + waves - 1) / waves;
-  rpw = ((rpw + GEMV_RG - 1) / GEMV_RG) * GEMV_RG;
-  const int blocks = (total + rpw * GEMV_WAVES - 1) / (rpw * GEMV_WAVES);
-  hipLaunchKernelGGL((gemv_bf16_kernel<NB, KC>), dim3(blocks), dim3(256), 0, st, g, x, K, silu_in ? 1 : 0, total, rpw);
+  // no more blocks than there are row groups
+  const int groups = (total + GEMV_RG - 1) / GEMV_RG;
+  const int need = (groups + GEMV_WAVES - 1) / GEMV_WAVES;
+  const int blocks = need < cus * GEMV_BLOCKS_PER_CU ? need : cus * GEMV_BLOCKS_PER_CU;
+  hipLaunchKernelGGL((gemv_bf16_kernel<NB, KC>), dim3(blocks), dim3(256), 0, st, g, x, K, silu_in ? 1 : 0, total);
   return hipGetLastError();
 }
 
