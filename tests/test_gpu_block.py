@@ -141,6 +141,13 @@ def test_block_bf16_sharp_full_1024():
     run_case("bf16", 1, 64, 64, 512, variant="sharp")
 
 
+def test_block_bf16_cfg_batch_masked_full_1024():
+    """The cond + uncond shape (B = 2, 4096 image + 512 text tokens) with the
+    second sample's text cut to 77 keys (its last key tile partly masked,
+    its padded text queries excluded)."""
+    run_case("bf16", 2, 64, 64, 512, txt_len=[512, 77])
+
+
 # ------------------------------------------------------------ robustness
 def _block_setup(B=2, gh=10, gw=13, St=45, txt_len=(45, 17)):
     dv = _dev()
@@ -171,6 +178,25 @@ def test_block_nan_poisoned_workspace_gives_identical_output():
     assert np.all(np.isfinite(outs[0][0]))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1][0], outs[1][1][0])
     assert np.array_equal(outs[0][1][1, :17], outs[1][1][1, :17])   # valid text rows of sample 1
+
+
+def test_block_nan_poisoned_workspace_full_1024_cfg_batch():
+    """The same at the full 1024^2 cond + uncond shape with masked text (the
+    benchmarked launch's tile counts and workspace layout): bit-identical
+    outputs."""
+    dv, cfg, blk, h_img, h_txt, args = _block_setup(2, 64, 64, 512, (512, 77))
+    outs = []
+    for fill in (0, 255):
+        ws = dv.Workspace()
+        buf = ws.get(dv.L.lens_block_workspace_bytes(cfg, 2, 4096, 512))
+        buf.fill_(fill)
+        hi, ht = dv.upload(h_img), dv.upload(h_txt)
+        dv.block_forward(cfg, blk, hi, ht, *args, ws)
+        torch.cuda.synchronize()
+        outs.append((hi.cpu().numpy(), ht.cpu().numpy()))
+    assert np.all(np.isfinite(outs[0][0]))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1][0], outs[1][1][0])
+    assert np.array_equal(outs[0][1][1, :77], outs[1][1][1, :77])
 
 
 def test_block_writes_nothing_outside_its_outputs():
