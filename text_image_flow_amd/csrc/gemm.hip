@@ -1194,7 +1194,29 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st, const Qk
   // gemm_bf16 loop at the 1024^2 CFG shape); the other epilogues keep
   // gemm_bf16, whose loop measured as fast or faster with them
   if constexpr (SWI) {
-    if (buf && !lens_gemm_pp_off()) return run_pp<EPI>(pr, np, st, qo);
+    if (buf && !lens_gemm_pp_off()) {
+      // A grouped (image, text) launch whose text tiles spill into a partial
+      // last round: the image problem alone in 256 x 256 tiles, then the
+      // text problem in 128 x 256 tiles, when the rounds that costs (a half
+      // tile takes ~0.68 of a full one) beat the grouped launch's.  At the
+      // 1024^2 CFG shape: 1024 image tiles (4 rounds on 256 CUs) + 128 text
+      // tiles (a fifth, half-empty round) become 4 rounds + one round of
+      // 256 half tiles.
+      if (np == 2 && pr[0].M > 0 && pr[1].M > 0) {
+        const int C = cu_count();
+        const int t0 = ((pr[0].M + 255) / 256) * (pr[0].N / outc);
+        const int t1 = ((pr[1].M + 255) / 256) * (pr[1].N / outc);
+        const int h1 = ((pr[1].M + 127) / 128) * (pr[1].N / outc);
+        const double grouped = (double)((t0 + t1 + C - 1) / C);
+        const double split = (double)((t0 + C - 1) / C) + 0.68 * (double)((h1 + C - 1) / C);
+        if (split + 0.2 < grouped) {
+          const hipError_t e = run_pp<EPI>(pr, 1, st, qo);
+          if (e != hipSuccess) return e;
+          return run_bf16<128, 256, 2, 4, EPI, 4, true>(pr + 1, 1, st, qo);
+        }
+      }
+      return run_pp<EPI>(pr, np, st, qo);
+    }
   }
   return buf ? run_bf16<256, 256, 2, 4, EPI, 4, true>(pr, np, st, qo) : run_bf16<256, 256, 2, 4, EPI>(pr, np, st, qo);
 }
