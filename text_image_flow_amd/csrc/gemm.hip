@@ -1004,8 +1004,8 @@ __global__ __launch_bounds__(512) void gemm_pp(GemmProblem p0, GemmProblem p1, i
 #undef PP_SETUP_W
 }
 
-// LENS_GEMM_PP=0 in the environment keeps the SwiGLU projection on
-// gemm_bf16 (for side-by-side measurement); read once.
+// LENS_GEMM_PP=0 in the environment keeps the SwiGLU and gated residual
+// projections on gemm_bf16 (for side-by-side measurement); read once.
 bool lens_gemm_pp_off() {
   static const bool off = [] {
     const char *e = getenv("LENS_GEMM_PP");
@@ -1191,8 +1191,7 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st, const Qk
   if (tiles256 * 2 < cu_count())
     return buf ? run_bf16<128, 256, 2, 4, EPI, 4, true>(pr, np, st, qo) : run_bf16<128, 256, 2, 4, EPI>(pr, np, st, qo);
   // w1 | w3 with the SwiGLU epilogue: the ping-pong kernel (1.09-1.15x the
-  // gemm_bf16 loop at the 1024^2 CFG shape); the other epilogues keep
-  // gemm_bf16, whose loop measured as fast or faster with them
+  // gemm_bf16 loop at the 1024^2 CFG shape)
   if constexpr (SWI) {
     if (buf && !lens_gemm_pp_off()) {
       // A grouped (image, text) launch whose text tiles spill into a partial
@@ -1217,6 +1216,12 @@ hipError_t dispatch_bf16(const GemmProblem *pr, int np, hipStream_t st, const Qk
       }
       return run_pp<EPI>(pr, np, st, qo);
     }
+  }
+  // the gated residual GEMMs (out-proj, w2) also run on the ping-pong loop
+  // (measured 0.9 % faster per GEMM launch on the step; QKV stays on
+  // gemm_bf16, 0.5 % slower there)
+  if constexpr (EPI == EPI_GATED) {
+    if (buf && !lens_gemm_pp_off()) return run_pp<EPI>(pr, np, st, qo);
   }
   return buf ? run_bf16<256, 256, 2, 4, EPI, 4, true>(pr, np, st, qo) : run_bf16<256, 256, 2, 4, EPI>(pr, np, st, qo);
 }
