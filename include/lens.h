@@ -279,9 +279,11 @@ lens_status lens_quantize_mxfp8(const void *src, int32_t src_dtype, int64_t rows
  * later launch of the kernel families whose bit (1 << lens_kernel_kind) is
  * set record a pair of HIP events around itself, on the stream it is
  * launched on.  lens_timer_stop(ms, launches) synchronises those events,
- * writes the summed kernel milliseconds and launch counts per family into
- * ms[LENS_KERNEL_COUNT] and launches[LENS_KERNEL_COUNT] (either may be
- * NULL), and switches the timer off.  The timer state is per calling
+ * writes the summed kernel milliseconds and kernel launch counts per family
+ * into ms[LENS_KERNEL_COUNT] and launches[LENS_KERNEL_COUNT] (either may be
+ * NULL), and switches the timer off.  A call that launches two kernels of a
+ * family back to back (the w1 | w3 GEMM may) records one span and counts
+ * two launches.  The timer state is per calling
  * thread: start and stop on the thread that makes the timed calls.
  */
 typedef enum {

@@ -39,6 +39,7 @@ struct Timer {
   uint32_t mask = 0;
   std::vector<hipEvent_t> pool;
   std::vector<int> kind_of;  // family of each recorded event pair
+  std::vector<int> kernels;  // kernels launched inside each pair
   size_t used = 0;
 };
 thread_local Timer g_timer;
@@ -59,12 +60,17 @@ struct Timed {
       g_timer.pool.push_back(e);
     }
     g_timer.kind_of.push_back((int)k);
+    g_timer.kernels.push_back(1);
     e0 = g_timer.pool[g_timer.used++];
     e1 = g_timer.pool[g_timer.used++];
     (void)hipEventRecord(e0, st);
   }
-  hipError_t done(hipError_t e) {
-    if (on) (void)hipEventRecord(e1, st);
+  // `kernels`: how many kernels the timed call launched (one span of time)
+  hipError_t done(hipError_t e, int kernels = 1) {
+    if (on) {
+      (void)hipEventRecord(e1, st);
+      g_timer.kernels.back() = kernels;
+    }
     return e;
   }
 };
@@ -236,7 +242,8 @@ DitWs carve_dit(const lens_config *c, int B, int Si, int St, char *base) {
 // ------------------------------------------------------------ launches
 lens_status gemm(lens_kernel_kind, int epi, bool bf, GemmProblem *p, int np, hipStream_t st) {
   Timed t(LENS_KERNEL_GEMM, st);
-  hipError_t e = t.done(launch_gemm(epi, bf, p, np, st));
+  const hipError_t r = launch_gemm(epi, bf, p, np, st);
+  hipError_t e = t.done(r, gemm_kernels_launched());
   if (e != hipSuccess) return fail(LENS_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
   return LENS_OK;
 }
@@ -257,7 +264,8 @@ void to_fp8(GemmProblem *g, const lens_linear &li, const lens_linear &lt, const 
 
 lens_status gemm8(int epi, GemmProblem *p, hipStream_t st, const QkvOut *qo = nullptr) {
   Timed t(LENS_KERNEL_GEMM, st);
-  hipError_t e = t.done(launch_gemm_fp8(epi, p, 2, st, qo));
+  const hipError_t r = launch_gemm_fp8(epi, p, 2, st, qo);
+  hipError_t e = t.done(r, gemm_kernels_launched());
   if (e != hipSuccess) return fail(LENS_ERR_HIP, "fp8 GEMM launch failed: %s", hipGetErrorString(e));
   return LENS_OK;
 }
@@ -320,7 +328,8 @@ lens_status block_core(const lens_config *c, const lens_block_w *w, float *h_img
       LTRY(gemm8(EPI_QKV, g, st, &qo));
     } else {
       Timed t(LENS_KERNEL_GEMM, st);
-      e = t.done(launch_gemm(EPI_QKV, true, g, 2, st, &qo));
+      e = launch_gemm(EPI_QKV, true, g, 2, st, &qo);
+      e = t.done(e, gemm_kernels_launched());
       if (e != hipSuccess) return fail(LENS_ERR_HIP, "QKV GEMM launch failed: %s", hipGetErrorString(e));
     }
   } else {
@@ -697,6 +706,7 @@ lens_status lens_timer_start(uint32_t mask) {
   g_timer.mask = mask;
   g_timer.used = 0;
   g_timer.kind_of.clear();
+  g_timer.kernels.clear();
   return LENS_OK;
 }
 
@@ -711,9 +721,10 @@ lens_status lens_timer_stop(double *ms, int64_t *launches) {
     float f = 0.f;
     HIP_TRY(hipEventElapsedTime(&f, g_timer.pool[2 * i], g_timer.pool[2 * i + 1]));
     acc[g_timer.kind_of[i]] += f;
-    cnt[g_timer.kind_of[i]] += 1;
+    cnt[g_timer.kind_of[i]] += g_timer.kernels[i];
   }
   g_timer.kind_of.clear();
+  g_timer.kernels.clear();
   for (int k = 0; k < LENS_KERNEL_COUNT; ++k) {
     if (ms) ms[k] = acc[k];
     if (launches) launches[k] = cnt[k];

@@ -114,6 +114,8 @@ struct QkvOut {
 // (qo: EPI_QKV only).
 hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream,
                        const QkvOut *qo = nullptr);
+// Kernels the calling thread's last launch_gemm / launch_gemm_fp8 issued.
+int gemm_kernels_launched();
 
 // The same grouped GEMM on MX fp8 operands (e4m3 elements, E8M0 scales per
 // 32 along K; K % 128 == 0); the epilogues are those of the bf16 path.

@@ -1016,6 +1016,10 @@ bool lens_gemm_pp_off() {
 
 // Persistent launch: at most one workgroup per CU, a multiple of 8 so that
 // every XCD gets the same number of workgroups.
+// GEMM kernels launched by the current thread's last launch_gemm /
+// launch_gemm_fp8 call (a call may split into two launches).
+thread_local int g_gemm_kernels = 0;
+
 int cu_count() {
   static int n[16] = {0};
   int dev = 0;
@@ -1060,6 +1064,7 @@ hipError_t run_bf16(const GemmProblem *pr, int np, hipStream_t st, const QkvOut 
     if (!qo) return hipErrorInvalidValue;
     qv = *qo;
   }
+  ++g_gemm_kernels;
   hipLaunchKernelGGL((gemm_bf16<BM, BN, WM, WN, EPI, GM, BUF, F8>), dim3(grid), dim3(64 * WM * WN), 0, st, q0, q1, tiles[0],
                      ntm[0] > 0 ? ntm[0] : 1, ntm[1] > 0 ? ntm[1] : 1, total, per_xcd, qv);
   return hipGetLastError();
@@ -1090,6 +1095,7 @@ hipError_t run_pp(const GemmProblem *pr, int np, hipStream_t st, const QkvOut *q
     if (!qo) return hipErrorInvalidValue;
     qv = *qo;
   }
+  ++g_gemm_kernels;
   hipLaunchKernelGGL((gemm_pp<EPI, GM>), dim3(grid), dim3(512), 0, st, q0, q1, tiles[0], ntm[0] > 0 ? ntm[0] : 1,
                      ntm[1] > 0 ? ntm[1] : 1, total, per_xcd, qv);
   return hipGetLastError();
@@ -1160,6 +1166,7 @@ hipError_t run_f32(const GemmProblem *pr, int np, hipStream_t st) {
   const int total = tiles[0] + tiles[1];
   if (total == 0) return hipSuccess;
   GemmProblem q1 = np > 1 ? pr[1] : pr[0];
+  ++g_gemm_kernels;
   hipLaunchKernelGGL((gemm_f32_simple<EPI>), dim3(total), dim3(256), 0, st, pr[0], q1, tiles[0], ntm[0], ntm[1]);
   return hipGetLastError();
 }
@@ -1245,6 +1252,7 @@ hipError_t dispatch_fp8(const GemmProblem *pr, int np, hipStream_t st, const Qkv
 }
 
 hipError_t launch_gemm_fp8(int epi, const GemmProblem *probs, int nprob, hipStream_t stream, const QkvOut *qo) {
+  g_gemm_kernels = 0;
   switch (epi) {
     case EPI_STORE: return dispatch_fp8<EPI_STORE>(probs, nprob, stream, nullptr);
     case EPI_GATED: return dispatch_fp8<EPI_GATED>(probs, nprob, stream, nullptr);
@@ -1255,8 +1263,11 @@ hipError_t launch_gemm_fp8(int epi, const GemmProblem *probs, int nprob, hipStre
   return hipErrorInvalidValue;
 }
 
+int gemm_kernels_launched() { return g_gemm_kernels; }
+
 hipError_t launch_gemm(int epi, bool bf16_path, const GemmProblem *probs, int nprob, hipStream_t stream,
                        const QkvOut *qo) {
+  g_gemm_kernels = 0;
   if (bf16_path) {
     switch (epi) {
       case EPI_STORE: return dispatch_bf16<EPI_STORE>(probs, nprob, stream, nullptr);
