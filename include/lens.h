@@ -150,8 +150,9 @@ size_t lens_dit_workspace_bytes(const lens_config *cfg, int32_t B, int32_t S_img
  *         for every sample of the batch).
  *   txt_len [B] int32 valid text lengths (device), or NULL = all S_txt valid.
  *         Text keys j >= txt_len[b] are masked; values are clamped to
- *         [0, S_txt].  Rows of masked text queries are computed but their
- *         values are unspecified.
+ *         [0, S_txt].  Rows of masked text queries hold unspecified
+ *         values (their attention is skipped where a whole 128-query block
+ *         of them would be computed for nothing).
  * Per stream: a = RMSNorm(h)(1 + scale1) + shift1; qkv = a W_qkv^T + b;
  * q, k <- RMSNorm_64(.) * gain, then RoPE; joint softmax attention of each
  * sample's image and text queries over all of its valid keys, scale

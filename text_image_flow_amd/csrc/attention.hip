@@ -246,6 +246,10 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   const bf16 *Kg = (const bf16 *)a.K + bh * a.S_pad * 64;
   const bf16 *Vg = (const bf16 *)a.V + bh * a.S_pad * 64;
   const int n_kv = kv_count(a, b);
+  // a q-block holding only padded text queries (the sample's valid tokens,
+  // image and text, are its first n_kv): their rows are unspecified, so
+  // none of the block's work is needed
+  if (qb * 128 >= n_kv) return;
   const int n_tiles = (n_kv + KV_T - 1) / KV_T;
   const int n_full = n_kv / KV_T;
   const int hl = lane >> 5, ql = lane & 31;
