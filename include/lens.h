@@ -35,6 +35,11 @@
  *     workspace, sized by the *_workspace_bytes functions (256-byte aligned).
  *   - Matrices are row-major.  A Linear layer's weight is [out, in] (the
  *     input dimension contiguous) and its bias is [out] or NULL.
+ *   - Device tensors that the kernels access in 16-byte pieces must start on
+ *     a 16-byte boundary (torch allocations do): activations (x, txt_feats,
+ *     h_img, h_txt), outputs (v_out, q_out), every weight, bias, gain and
+ *     w_scale.  t, positions, txt_len and the flow-step vectors need only
+ *     their element alignment.  A misaligned tensor is LENS_ERR_INVALID_ARG.
  *   - Arguments and fields that name a lens_dtype or lens_status value are
  *     declared int32_t, so that any integer a caller passes is checked (an
  *     unknown value is LENS_ERR_INVALID_ARG) rather than read as an enum.

@@ -93,6 +93,8 @@ def _bad(cfg_mut=None, **kw):
     (None, {"ws_bytes": 100}, L.LENS_ERR_WORKSPACE, "workspace"),
     (None, {"ws": None}, L.LENS_ERR_WORKSPACE, "workspace"),
     (None, {"ws": 0x1001}, L.LENS_ERR_WORKSPACE, "aligned"),
+    (None, {"h_img": 0x1008}, L.LENS_ERR_INVALID_ARG, "16-byte aligned"),
+    (None, {"h_txt": 0x1004}, L.LENS_ERR_INVALID_ARG, "16-byte aligned"),
 ])
 def test_block_forward_argument_checks(mut, kw, status, frag):
     st, msg = _bad(mut, **kw)
@@ -106,6 +108,42 @@ def test_null_weight_is_rejected():
     assert st == L.LENS_ERR_INVALID_ARG and "NULL" in T.last_error()
     st = L.lib().lens_block_forward(None, None, None, None, None, None, None, None, 1, 1, 1, None, 0, None)
     assert st == L.LENS_ERR_INVALID_ARG and "cfg" in T.last_error()
+
+
+def test_misaligned_tensors_are_rejected_before_any_device_work():
+    """Tensors the kernels read in 16-byte pieces must start on a 16-byte
+    boundary: a weight, bias or gain that does not is an argument error (the
+    pointers are never dereferenced on the host)."""
+    def block_call(edit):
+        c = T.default_config(T.LENS_BF16)
+        w = T.LensBlockW()
+        for s in ("img", "txt"):
+            sw = getattr(w, s)
+            for n in ("mod", "qkv", "out", "w1", "w3", "w2"):
+                getattr(sw, n).w = 0x1000
+            sw.q_gain = sw.k_gain = 0x1000
+        edit(w)
+        st = T.lens_block_forward(c, w, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 1, 16, 8, 0x1000, 1 << 40,
+                                  None)
+        return st, T.last_error()
+
+    for edit, frag in ((lambda w: setattr(w.txt.w2, "w", 0x1002), "txt.w2"),
+                       (lambda w: setattr(w.img.qkv, "b", 0x1008), "img.qkv"),
+                       (lambda w: setattr(w.img, "k_gain", 0x1002), "gains")):
+        st, msg = block_call(edit)
+        assert st == L.LENS_ERR_INVALID_ARG and "16-byte aligned" in msg and frag in msg, (st, msg)
+    # the denoiser's inputs and output, and the quantizer's source
+    c = T.default_config(T.LENS_BF16)
+    c.n_blocks = 0
+    d = T.LensDitW()
+    for n in ("t_fc1", "t_fc2", "img_in", "txt_in", "norm_out", "proj_out"):
+        getattr(d, n).w = 0x1000
+    d.txt_gain = 0x1000
+    for x, f, v in ((0x1001, 0x1000, 0x1000), (0x1000, 0x1004, 0x1000), (0x1000, 0x1000, 0x100c)):
+        st = T.lens_dit_forward(c, d, x, f, 0x1000, 0x1000, 0x1000, None, 1, 16, 8, v, 0x1000, 1 << 40, None)
+        assert st == L.LENS_ERR_INVALID_ARG and "16-byte aligned" in T.last_error(), T.last_error()
+    st = T.lens_quantize_mxfp8(0x1002, L.LENS_BF16, 4, 128, L.LENS_MX_SLABS, 0x1000, 0x1000, None)
+    assert st == L.LENS_ERR_INVALID_ARG and "16-byte aligned" in T.last_error()
 
 
 def test_dit_and_flow_argument_checks():

@@ -131,8 +131,15 @@ lens_status check_sizes(int B, int Si, int St) {
   return LENS_OK;
 }
 
+// Device tensors that kernels read or write with 16-byte vector or buffer
+// accesses (activations, weights, biases, scales, outputs) must start on a
+// 16-byte boundary; NULL passes.
+bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 lens_status check_linear(const lens_linear &l, const char *name) {
   if (!l.w) return fail(LENS_ERR_INVALID_ARG, "weight %s is NULL", name);
+  if (!al16(l.w) || !al16(l.b) || !al16(l.w_scale))
+    return fail(LENS_ERR_INVALID_ARG, "weight %s: w, b and w_scale must be 16-byte aligned", name);
   return LENS_OK;
 }
 
@@ -147,9 +154,14 @@ lens_status check_block_w(const lens_block_w *w, int idx, bool fp8) {
       if (!ls[j]->w) return fail(LENS_ERR_INVALID_ARG, "block %d %s.%s weight is NULL", idx, nm[i], ln[j]);
       if (fp8 && j > 0 && !ls[j]->w_scale)
         return fail(LENS_ERR_INVALID_ARG, "block %d %s.%s: gemm_fp8 needs w_scale", idx, nm[i], ln[j]);
+      if (!al16(ls[j]->w) || !al16(ls[j]->b) || !al16(ls[j]->w_scale))
+        return fail(LENS_ERR_INVALID_ARG, "block %d %s.%s: w, b and w_scale must be 16-byte aligned", idx, nm[i],
+                    ln[j]);
     }
     if (!s[i]->q_gain || !s[i]->k_gain)
       return fail(LENS_ERR_INVALID_ARG, "block %d %s q/k gain is NULL", idx, nm[i]);
+    if (!al16(s[i]->q_gain) || !al16(s[i]->k_gain))
+      return fail(LENS_ERR_INVALID_ARG, "block %d %s q/k gains must be 16-byte aligned", idx, nm[i]);
   }
   return LENS_OK;
 }
@@ -494,6 +506,7 @@ lens_status lens_block_forward(const lens_config *c, const lens_block_w *w, floa
   LTRY(check_block_w(w, 0, c->gemm_fp8));
   if (!h_img || !temb || !img_pos) return fail(LENS_ERR_INVALID_ARG, "h_img, temb and img_pos must not be NULL");
   if (St > 0 && (!h_txt || !txt_pos)) return fail(LENS_ERR_INVALID_ARG, "h_txt and txt_pos must not be NULL");
+  if (!al16(h_img) || !al16(h_txt)) return fail(LENS_ERR_INVALID_ARG, "h_img and h_txt must be 16-byte aligned");
   const BlockWs need = carve_block(c, B, Si, St, nullptr, true);
   if (!workspace || ws_bytes < need.bytes)
     return fail(LENS_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? ws_bytes : 0, need.bytes);
@@ -525,11 +538,14 @@ lens_status check_dit_call(const lens_config *c, const lens_dit_w *w, const void
   LTRY(check_linear(w->norm_out, "norm_out"));
   LTRY(check_linear(w->proj_out, "proj_out"));
   if (!w->txt_gain) return fail(LENS_ERR_INVALID_ARG, "txt_gain is NULL");
+  if (!al16(w->txt_gain)) return fail(LENS_ERR_INVALID_ARG, "txt_gain must be 16-byte aligned");
   if (c->n_blocks > 0 && !w->blocks) return fail(LENS_ERR_INVALID_ARG, "blocks is NULL");
   for (int i = 0; i < c->n_blocks; ++i) LTRY(check_block_w(&w->blocks[i], i, c->gemm_fp8));
   if (!x || !t || !img_pos || !v_out) return fail(LENS_ERR_INVALID_ARG, "x, t, img_pos and v_out must not be NULL");
   if (St > 0 && (!txt_feats || !txt_pos))
     return fail(LENS_ERR_INVALID_ARG, "txt_feats and txt_pos must not be NULL");
+  if (!al16(x) || !al16(txt_feats) || !al16(v_out))
+    return fail(LENS_ERR_INVALID_ARG, "x, txt_feats and v_out must be 16-byte aligned");
   return LENS_OK;
 }
 
@@ -694,6 +710,7 @@ lens_status lens_quantize_mxfp8(const void *src, int32_t src_dtype, int64_t rows
     return fail(LENS_ERR_INVALID_ARG, "rows %lld / cols %d: need rows >= 0 and cols a positive multiple of %d",
                 (long long)rows, (int)cols, unit);
   if (rows > 0 && (!src || !q_out || !scale_out)) return fail(LENS_ERR_INVALID_ARG, "NULL pointer");
+  if (!al16(src) || !al16(q_out)) return fail(LENS_ERR_INVALID_ARG, "src and q_out must be 16-byte aligned");
   if (rows > (((int64_t)1 << 40) / cols)) return fail(LENS_ERR_UNSUPPORTED, "too many elements");
   MxQuantProblem q{src, q_out, scale_out, rows};
   HIP_TRY(launch_mx_quant(&q, 1, cols, src_dtype == LENS_BF16, scale_layout == LENS_MX_SLABS,

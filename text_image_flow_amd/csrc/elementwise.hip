@@ -524,15 +524,52 @@ __global__ void timestep_kernel(const float *t, float *phi, int B, int dim, floa
 }
 
 // ------------------------------------------------ text feature RMSNorm
-// One block per token row; wave w normalises layers w, w+4, ...
+// One block per token row; wave w normalises layers w, w+4, ...  When the
+// layer width F splits into 16-byte chunks and a lane's share of them fits
+// TXT_CHUNKS, the lane loads its chunks once (16 bytes each) and keeps them
+// in registers for the second pass; otherwise element by element.
+constexpr int TXT_CHUNKS = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void txt_norm_kernel(const T *feats, const T *gain, T *out, int layers, int F,
                                                        float eps) {
+  constexpr int VEC = 16 / sizeof(T);
+  typedef T vecT __attribute__((ext_vector_type(VEC)));
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = F % VEC == 0 ? F / VEC : 0;
+  const bool vec = nch > 0 && nch <= 64 * TXT_CHUNKS;
   for (int l = wave; l < layers; l += 4) {
     const T *x = feats + ((int64_t)row * layers + l) * F;
     T *y = out + ((int64_t)row * layers + l) * F;
+    const T *g = gain + (int64_t)l * F;
+    if (vec) {
+      vecT v[TXT_CHUNKS];
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < TXT_CHUNKS; ++c) {
+        const int ch = c * 64 + lane;
+        if (ch < nch) {
+          v[c] = *(const vecT *)(x + ch * VEC);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) ss += to_f32(v[c][e]) * to_f32(v[c][e]);
+        }
+      }
+      ss = wave_sum(ss);
+      const float r = rsqrtf(ss / (float)F + eps);
+#pragma unroll
+      for (int c = 0; c < TXT_CHUNKS; ++c) {
+        const int ch = c * 64 + lane;
+        if (ch < nch) {
+          const vecT gv = *(const vecT *)(g + ch * VEC);
+          vecT o;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[e] = from_f32<T>(to_f32(v[c][e]) * r * to_f32(gv[e]));
+          *(vecT *)(y + ch * VEC) = o;
+        }
+      }
+      continue;
+    }
     float ss = 0.f;
     for (int i = lane; i < F; i += 64) {
       const float v = to_f32(x[i]);
@@ -540,7 +577,7 @@ __global__ __launch_bounds__(256) void txt_norm_kernel(const T *feats, const T *
     }
     ss = wave_sum(ss);
     const float r = rsqrtf(ss / (float)F + eps);
-    for (int i = lane; i < F; i += 64) y[i] = from_f32<T>(to_f32(x[i]) * r * to_f32(gain[(int64_t)l * F + i]));
+    for (int i = lane; i < F; i += 64) y[i] = from_f32<T>(to_f32(x[i]) * r * to_f32(g[i]));
   }
 }
 
