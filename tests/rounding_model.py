@@ -2,6 +2,11 @@
 round-to-nearest-even inserted at every point where the HIP path stores a
 bf16 tensor, and nothing else changed.
 
+The whole-model variant (dit_forward_rounded) adds the two bf16 storage
+points outside the blocks: the normalised text features before txt_in and
+the norm_out-modulated image rows before proj_out (the latent x arrives in
+bf16 already; temb, the modulations and the residual stream stay float).
+
 Test infrastructure only (CPU).  It shows how far from the exact block a
 computation can land that differs from it only by those storage roundings,
 which is what the GPU parity bars for bf16 block outputs and deltas are
@@ -15,7 +20,7 @@ storage points are those of the bf16 kernels:
   k   = RoPE(RMSNorm_64(k) g_k)                  -> bf16
   v                                              -> bf16
   p   = 2^(s - m)                                -> bf16 (the PV product's
-        operand; the row sum adds the same bf16 values)
+        operand; the row sum adds the unrounded values)
   O   = sum(p v) / sum(p)                        -> bf16
   u   = SiLU(W1 a + b1)(W3 a + b3)               -> bf16 (SwiGLU epilogue)
   residual updates h += gate * (.) stay float (fp32 on the GPU).
@@ -42,14 +47,15 @@ def bf16(x):
 
 def _attention_rounded(q2, k, v, key_valid):
     """q2 in log2 units (already rounded), k, v rounded; probabilities
-    rounded to bf16 before both the product with V and the row sum."""
+    rounded to bf16 before the product with V, while the row sum adds them
+    unrounded."""
     Sq, H, d = q2.shape
     out = np.empty((Sq, H, d))
     for h in range(H):
         s = q2[:, h, :] @ k[:, h, :].T
         s[:, ~key_valid] = -np.inf
-        p = bf16(np.exp2(s - s.max(axis=1, keepdims=True)))
-        out[:, h, :] = (p @ v[:, h, :]) / p.sum(axis=1, keepdims=True)
+        e = np.exp2(s - s.max(axis=1, keepdims=True))
+        out[:, h, :] = (bf16(e) @ v[:, h, :]) / e.sum(axis=1, keepdims=True)
     return out
 
 
@@ -136,3 +142,51 @@ def budget_model_block(block=0, t=0.75):
         res["out"] = max(res["out"], err / float(np.sqrt(np.mean(x_ * x_))))
         res["delta"] = max(res["delta"], err / float(np.sqrt(np.mean((x_ - h_) ** 2))))
     return res
+
+
+def dit_forward_rounded(top, blocks, x, feats, t, img_pos, txt_pos, txt_len=None, *, layers=4, eps=1e-6):
+    """The oracle denoiser (oracle.dit_forward) with the bf16 storage points
+    of the blocks (block_forward_rounded) and of the text-feature norm and
+    the final layer's modulation; same arguments and output (float64)."""
+    temb = O.timestep_embedding(top, t)
+    h_img = O.linear(x, top["img_in_w"], top.get("img_in_b"))
+    f = np.asarray(feats, np.float64)
+    F = f.shape[-1] // layers
+    tn = bf16(np.concatenate([O.rms_norm(f[..., l * F:(l + 1) * F], eps, top["txt_gain"][l]) for l in range(layers)],
+                             -1))
+    h_txt = O.linear(tn, top["txt_in_w"], top.get("txt_in_b"))
+    for wb in blocks:
+        h_img, h_txt = block_forward_rounded(wb, h_img, h_txt, temb, img_pos, txt_pos, txt_len, eps=eps)
+    m = O.linear(O.silu(temb), top["norm_out_w"], top.get("norm_out_b"))
+    D = m.shape[-1] // 2
+    a = bf16(O.modulate(O.rms_norm(h_img, eps), m[:, :D], m[:, D:]))
+    return O.linear(a, top["proj_out_w"], top.get("proj_out_b"))
+
+
+def budget_sampler_step(norm_rescale=False, mu=None, steps=3, scale=5.0, gh=8, gw=8, St=16, n_blocks=2):
+    """Max |dx_rounded - dx_exact| / RMS(dx_exact) over the steps of a CFG
+    Euler run (one latent, cond + uncond text in one B = 2 call, the seeded
+    model cut to n_blocks blocks): at each step the velocities of
+    dit_forward_rounded and of the oracle at the same bf16 input, combined
+    by the plain or norm-rescaled CFG step; the trajectory is the oracle's."""
+    top = synth.top_weights()
+    blocks = [synth.block_weights(i) for i in range(n_blocks)]
+    feats = np.concatenate([synth.text_features(1, St, seed=synth.SEED_TEXT_COND),
+                            synth.text_features(1, St, seed=synth.SEED_TEXT_UNCOND)])
+    ip, tp = synth.image_positions(gh, gw), synth.text_positions(St)
+    x = np.asarray(synth.latents(1, gh * gw), np.float64)[0]
+    ts = O.time_grid(steps, mu=mu)
+    step = O.flow_step_rescaled if norm_rescale else O.flow_step
+    worst = 0.0
+    for k in range(steps):
+        xa = np.stack([synth.bf16_round(x.astype(np.float32))] * 2)
+        t = np.array([ts[k], ts[k]])
+        dt = ts[k + 1] - ts[k]
+        ve = O.dit_forward(top, blocks, xa, feats, t, ip, tp)
+        vr = dit_forward_rounded(top, blocks, xa, feats, t, ip, tp)
+        xe = step(x, ve[0], ve[1], dt, scale)
+        xr = step(x, vr[0], vr[1], dt, scale)
+        dxe = xe - x
+        worst = max(worst, float(np.max(np.abs(xr - xe))) / float(np.sqrt(np.mean(dxe * dxe))))
+        x = xe
+    return worst

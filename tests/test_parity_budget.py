@@ -8,8 +8,9 @@ and the canonical bars must stay within 2.5x of it, so they cannot drift
 loose unnoticed.  CPU only."""
 import pytest
 
-from tests.parity import DELTA_REL, LATE_DELTA_REL, LATE_OUT_REL, MAXABS_REL, MODEL_DELTA_REL, SHARP_DELTA_REL
-from tests.rounding_model import budget, budget_model_block
+from tests.parity import (DELTA_REL, LATE_DELTA_REL, LATE_OUT_REL, MAXABS_REL, MODEL_DELTA_REL, SAMPLER_DX_REL,
+                          SHARP_DELTA_REL)
+from tests.rounding_model import budget, budget_model_block, budget_sampler_step
 
 # (name, variant, B, grid h, grid w, S_txt, txt_len, biases, out bar, delta bar, tight)
 CASES = [
@@ -48,6 +49,17 @@ def test_model_block_bar_covers_rounding_budget():
     print(msg)
     assert MAXABS_REL >= 1.25 * b["out"] and MODEL_DELTA_REL >= 1.25 * b["delta"], msg
     assert MODEL_DELTA_REL <= 2.5 * b["delta"], msg
+
+
+@pytest.mark.parametrize("norm_rescale,mu", [(False, None), (True, 1.06)], ids=["plain", "rescaled-shifted"])
+def test_sampler_increment_bar_covers_rounding_budget(norm_rescale, mu):
+    """The teacher-forced CFG sampler checks (2 blocks, 8x8 latent, 16 text
+    tokens, scale 5, three steps): the increment bar against the
+    whole-model budget, same margins as the block bars."""
+    b = budget_sampler_step(norm_rescale, mu)
+    msg = f"sampler dx: budget {b:.4f}; bar {SAMPLER_DX_REL} (margin {SAMPLER_DX_REL / b:.2f})"
+    print(msg)
+    assert 1.25 * b <= SAMPLER_DX_REL <= 2.5 * b, msg
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])

@@ -23,7 +23,8 @@
 //     one query per lane, so the online-softmax rescale is a per-lane scalar;
 //   * Q arrives pre-scaled by scale * log2(e), and the QK MFMAs start from
 //     -m, so p = exp2(s) with no subtraction; the running max is lazy and
-//     row sums add the bf16 probabilities with v_dot2;
+//     row sums add the fp32 probabilities with plain adds (the PV product
+//     takes them rounded to bf16);
 //   * the grid is flat and XCD-aware (one head's q-blocks share an L2);
 //   * O is written as bf16 rows, or (MX fp8 projections) as e4m3 rows with
 //     one E8M0 scale per 32 dims, quantized from fp32 in registers.
@@ -141,7 +142,6 @@ template <bool FIRST, bool MASK, bool BOUNDED>
 __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, const bf16x8 (&qf)[4], f32x16 (&o)[2],
                                              float &m_run, float &l_run, f32x16 &minit, int kv0, int n_kv, int ql,
                                              int hl) {
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
   const int vlane = hl * 32 + ql;
   const int sw = (ql >> 1) & 7;   // rows ql and 32 + ql share the swizzle
   // keys 0-31 (s0) fully before keys 32-63 (s1), so that in the bounded
@@ -204,7 +204,12 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
   }
   }
   // probabilities of keys 0-31 (P^T k steps 0, 1), their PV MFMAs, then
-  // keys 32-63 (k steps 2, 3)
+  // keys 32-63 (k steps 2, 3).  The PV product takes them rounded to bf16;
+  // the row sum adds their fp32 values with plain adds, which issue
+  // alongside another wave's MFMAs (measured on MI355X: v_add_f32 from a
+  // second wave of the SIMD overlaps MFMA work fully, v_dot2_f32_bf16 not at
+  // all).  One add chain: a second one costs the registers that keep three
+  // waves per SIMD.
   bf16x8 pb[4];
   float lsum = l_run;   // the row sum continues the running sum directly
 #pragma unroll
@@ -212,10 +217,14 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
     const f32x16 &sh = half ? s1 : s0;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      bf16x2 p0 = {(bf16)__builtin_amdgcn_exp2f(sh[e]), (bf16)__builtin_amdgcn_exp2f(sh[e + 1])};
-      bf16x2 p1 = {(bf16)__builtin_amdgcn_exp2f(sh[8 + e]), (bf16)__builtin_amdgcn_exp2f(sh[9 + e])};
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, lsum, false);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, lsum, false);
+      const float x0 = __builtin_amdgcn_exp2f(sh[e]), x1 = __builtin_amdgcn_exp2f(sh[e + 1]);
+      const float x2 = __builtin_amdgcn_exp2f(sh[8 + e]), x3 = __builtin_amdgcn_exp2f(sh[9 + e]);
+      bf16x2 p0 = {(bf16)x0, (bf16)x1};
+      bf16x2 p1 = {(bf16)x2, (bf16)x3};
+      lsum += x0;
+      lsum += x1;
+      lsum += x2;
+      lsum += x3;
       pb[2 * half][e] = p0[0]; pb[2 * half][e + 1] = p0[1];
       pb[2 * half + 1][e] = p1[0]; pb[2 * half + 1][e + 1] = p1[1];
     }
@@ -230,7 +239,8 @@ __device__ __forceinline__ void attn_tile(const char *sKb, const char *sVb, cons
   l_run = lsum;
 }
 
-__global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
+// three waves per SIMD (168 VGPRs) are what the tile loop is scheduled for
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bf16(AttnArgs a) {
   constexpr int TILE_BYTES = 64 * 128;        // K tile or V tile (row-major)
   constexpr int STAGE = 2 * TILE_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
