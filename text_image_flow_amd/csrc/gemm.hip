@@ -964,15 +964,23 @@ __global__ __launch_bounds__(512) void gemm_pp(GemmProblem p0, GemmProblem p1, i
       else wait_vm<0>();
     }
     PP_BARRIER();
-    // ---- compute phase of slab s
+    // ---- compute phase of slab s (a tile's first k step starts its
+    // accumulators from zero in the MFMA itself, not from 128 moves)
     if (ckt == 0) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][j], fa[0][i], f32x16{}, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 1; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
