@@ -196,11 +196,14 @@ do {                                                                            
         for (int k = 0; k < 16; ++k) gw[j][k] = gp_[k];
       }
     }
+    // Two passes, so that no wait for the RoPE table stands behind stores:
+    // first every row tile is normalised, rotated and packed in registers
+    // (its 8 table loads issued together), then all of them are stored.
+    u32x4 packed[MT][2][2];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int m = m0 + wm * WTM + i * 32 + frow;
-      const bool ok = m < M;
-      const int mc = ok ? m : 0;
+      const int mc = m < M ? m : 0;
       const int bsmp = mc / rps, joint = joff + (mc - bsmp * rps);
       float y[2][4][4];
 #pragma unroll
@@ -213,6 +216,14 @@ do {                                                                            
           for (int e = 0; e < 4; ++e) y[j][q][e] = acc[i][j][4 * q + e] + b[e];
         }
       if (sect < 2) {
+        // this lane's rotation pairs j*16 + 4q + 2hl and the next one, as
+        // float4 (cos, sin, cos, sin) index j*8 + 2q + hl of the token's row
+        const float4 *rope = (const float4 *)(qo.rope + (int64_t)joint * 32);
+        float4 cs[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cs[j][q] = rope[j * 8 + 2 * q + hl];
         // RMSNorm over the head (the partner lane holds the other half)
         float ss = 0.f;
 #pragma unroll
@@ -223,25 +234,21 @@ do {                                                                            
             for (int e = 0; e < 4; ++e) ss = fmaf(y[j][q][e], y[j][q][e], ss);
         const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
         const float r = rsqrtf((__uint_as_float(sw_[0]) + __uint_as_float(sw_[1])) / 64.f + qo.eps);
-        const float4 *rope = (const float4 *)(qo.rope + (int64_t)joint * 32);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             float g[4];
             BIAS4(gw[j], j, q, g);
-            // rotation pairs (j*32 + 8q + 4hl)/2 and the next one
-            const float4 cs = rope[(j * 16 + 4 * q + 2 * hl) >> 1];
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
-              const float c = e ? cs.z : cs.x, sn = e ? cs.w : cs.y;
+              const float c = e ? cs[j][q].z : cs[j][q].x, sn = e ? cs[j][q].w : cs[j][q].y;
               const float a0 = y[j][q][e] * r * g[e], a1 = y[j][q][e + 1] * r * g[e + 1];
               y[j][q][e] = (a0 * c - a1 * sn) * osc;
               y[j][q][e + 1] = (a0 * sn + a1 * c) * osc;
             }
           }
       }
-      bf16 *row = dst + (((int64_t)bsmp * qo.H + hh) * qo.S_pad + joint) * 64;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         unsigned pk[4][2];
@@ -251,10 +258,19 @@ do {                                                                            
           pk[q][1] = pack_bf2(y[j][q][2], y[j][q][3]);
         }
 #pragma unroll
-        for (int q = 0; q < 4; q += 2) {
-          const u32x4 o = pair_runs(pk[q][0], pk[q][1], pk[q + 1][0], pk[q + 1][1]);
-          if (ok) *(u32x4 *)(row + j * 32 + 8 * q + 8 * hl) = o;
-        }
+        for (int q = 0; q < 4; q += 2) packed[i][j][q / 2] = pair_runs(pk[q][0], pk[q][1], pk[q + 1][0], pk[q + 1][1]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + wm * WTM + i * 32 + frow;
+      if (m < M) {
+        const int bsmp = m / rps, joint = joff + (m - bsmp * rps);
+        bf16 *row = dst + (((int64_t)bsmp * qo.H + hh) * qo.S_pad + joint) * 64;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; q += 2) *(u32x4 *)(row + j * 32 + 8 * q + 8 * hl) = packed[i][j][q / 2];
       }
     }
   } else {
