@@ -273,19 +273,61 @@ do {                                                                            
           for (int q = 0; q < 4; q += 2) *(u32x4 *)(row + j * 32 + 8 * q + 8 * hl) = packed[i][j][q / 2];
       }
     }
+  } else if constexpr (EPI == EPI_GATED || EPI == EPI_STORE_F32) {
+    // fp32 outputs.  Per row tile, every load (gate and h rows: 16 float4)
+    // goes out before the first use, so the tile waits once, not once per
+    // float4 behind the stores before it; rows past M load row 0 and store
+    // nothing.
+    unsigned bw[H][16];
+#pragma unroll
+    for (int j = 0; j < H; ++j) LOAD_BIAS16(bias, j, bw[j]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + wm * WTM + i * 32 + frow;
+      const bool ok = m < M;
+      const int mc = ok ? m : 0;
+      float *hrow = (float *)C + (int64_t)mc * N + fw + 4 * hl;
+      float4 g4[H][4], h4[H][4];
+      if constexpr (EPI == EPI_GATED) {
+        const float *g = sec ? p1.gate : p0.gate;
+        const int rpg = sec ? p1.rows_per_gate : p0.rows_per_gate;
+        const int gst = sec ? p1.gate_stride : p0.gate_stride;
+        const float *grow = g + (int64_t)(mc / rpg) * gst + fw + 4 * hl;
+#pragma unroll
+        for (int j = 0; j < H; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            g4[j][q] = *(const float4 *)(grow + j * 32 + 8 * q);
+            h4[j][q] = *(const float4 *)(hrow + j * 32 + 8 * q);
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < H; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float b[4];
+          BIAS4(bw[j], j, q, b);
+          float4 y;
+          y.x = acc[i][j][4 * q + 0] + b[0];
+          y.y = acc[i][j][4 * q + 1] + b[1];
+          y.z = acc[i][j][4 * q + 2] + b[2];
+          y.w = acc[i][j][4 * q + 3] + b[3];
+          if constexpr (EPI == EPI_GATED) {
+            float4 o = h4[j][q];
+            o.x += g4[j][q].x * y.x;
+            o.y += g4[j][q].y * y.y;
+            o.z += g4[j][q].z * y.z;
+            o.w += g4[j][q].w * y.w;
+            y = o;
+          }
+          if (ok) *(float4 *)(hrow + j * 32 + 8 * q) = y;
+        }
+    }
   } else {
-  const float *gate_row = nullptr;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int m = m0 + wm * WTM + i * 32 + frow;
     const bool ok = m < M;
-    if constexpr (EPI == EPI_GATED) {
-      const GemmProblem &pg = p0;   // gate layout is shared by both problems
-      const float *g = sec ? p1.gate : pg.gate;
-      const int rpg = sec ? p1.rows_per_gate : p0.rows_per_gate;
-      const int gst = sec ? p1.gate_stride : p0.gate_stride;
-      gate_row = g + (int64_t)((ok ? m : 0) / rpg) * gst;
-    }
 #pragma unroll
     for (int j = 0; j < H; ++j) {
       const int f0 = fw + j * 32 + 4 * hl;     // + 8q
@@ -320,7 +362,7 @@ do {                                                                            
           if (hl == 0) ((unsigned char *)(sec ? p1.C_scale : p0.C_scale))[mx_scale_index(m, f / 32, M)] =
               (unsigned char)(ex + 127);
         }
-      } else if constexpr (EPI == EPI_STORE || EPI == EPI_SWIGLU) {
+      } else {
         unsigned pk[4][2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -343,31 +385,6 @@ do {                                                                            
         for (int q = 0; q < 4; q += 2) {
           const u32x4 o = pair_runs(pk[q][0], pk[q][1], pk[q + 1][0], pk[q + 1][1]);
           if (ok) *(u32x4 *)((bf16 *)C + (int64_t)m * N + (f0 - 4 * hl) + 8 * q + 8 * hl) = o;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float b[4];
-          BIAS4(bw, j, q, b);
-          float4 y;
-          y.x = acc[i][j][4 * q + 0] + b[0];
-          y.y = acc[i][j][4 * q + 1] + b[1];
-          y.z = acc[i][j][4 * q + 2] + b[2];
-          y.w = acc[i][j][4 * q + 3] + b[3];
-          float *dst = (float *)C + (int64_t)m * N + f0 + 8 * q;
-          if constexpr (EPI == EPI_STORE_F32) {
-            if (ok) *(float4 *)dst = y;
-          } else {
-            if (ok) {
-              const float4 g4 = *(const float4 *)(gate_row + f0 + 8 * q);
-              float4 h4 = *(float4 *)dst;
-              h4.x += g4.x * y.x;
-              h4.y += g4.y * y.y;
-              h4.z += g4.z * y.z;
-              h4.w += g4.w * y.w;
-              *(float4 *)dst = h4;
-            }
-          }
         }
       }
     }
